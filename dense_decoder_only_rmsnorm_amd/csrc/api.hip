@@ -1,0 +1,746 @@
+// C ABI of the Llama-3 decoder forward pass (declared in include/llama_mi355x.h):
+// argument validation, workspace carving and the launch sequence of each
+// entry point.  Everything is enqueued on the caller's stream; nothing here
+// allocates device memory or synchronises the host.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "kernels.h"
+#include "llama_mi355x.h"
+
+using namespace llk;
+using u16 = uint16_t;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIPCHK(expr)                                                                        \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess) return fail(LLAMA_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int kDecodeChunk = 256;  // keys per decode-attention chunk
+constexpr int kSkinnyRows = 64;    // rows per skinny GEMM launch
+
+// Model dimensions derived from llama_args.
+struct Dims {
+  int D, L, H, G, hd, F, V, nrep, dt, esz;
+  int Hq() const { return H * hd; }
+  int Hk() const { return G * hd; }
+  int Nqkv() const { return (H + 2 * G) * hd; }
+};
+
+int32_t ffn_hidden(const llama_args *a) {
+  // [P2 3.5]: hidden = int(2 * (4 * dim) / 3); times the multiplier when set
+  // (truncated); rounded up to a multiple of multiple_of.
+  int64_t hidden = (int64_t)(2.0 * (4.0 * a->dim) / 3.0);
+  if (a->ffn_dim_multiplier > 0.f) hidden = (int64_t)((double)a->ffn_dim_multiplier * (double)hidden);
+  const int64_t m = a->multiple_of;
+  const int64_t f = m * ((hidden + m - 1) / m);
+  return f > INT32_MAX ? -1 : (int32_t)f;
+}
+
+int check_model(const llama_args *a, Dims &d) {
+  if (!a) return fail(LLAMA_ERR_ARG, "args is NULL");
+  if (a->dim <= 0 || a->n_heads <= 0 || a->n_kv_heads <= 0 || a->n_layers < 0 || a->vocab_size <= 0 ||
+      a->multiple_of <= 0)
+    return fail(LLAMA_ERR_ARG, "non-positive dimension in llama_args");
+  if (a->dtype != LLAMA_F32 && a->dtype != LLAMA_BF16) return fail(LLAMA_ERR_ARG, "dtype %d is not F32/BF16", a->dtype);
+  if (!(a->norm_eps >= 0.f) || !(a->rope_theta > 0.f)) return fail(LLAMA_ERR_ARG, "norm_eps/rope_theta out of range");
+  if (a->dim % a->n_heads) return fail(LLAMA_ERR_SHAPE, "dim %d not divisible by n_heads %d", a->dim, a->n_heads);
+  if (a->n_heads % a->n_kv_heads)
+    return fail(LLAMA_ERR_SHAPE, "n_heads %d not divisible by n_kv_heads %d", a->n_heads, a->n_kv_heads);
+  d.D = a->dim;
+  d.L = a->n_layers;
+  d.H = a->n_heads;
+  d.G = a->n_kv_heads;
+  d.hd = a->dim / a->n_heads;
+  d.nrep = d.H / d.G;
+  d.V = a->vocab_size;
+  d.dt = a->dtype;
+  d.esz = a->dtype == LLAMA_BF16 ? 2 : 4;
+  d.F = ffn_hidden(a);
+  if (d.F <= 0) return fail(LLAMA_ERR_ARG, "ffn hidden size overflows");
+  if (d.hd % 2) return fail(LLAMA_ERR_SHAPE, "head_dim %d is odd (RoPE rotates pairs)", d.hd);
+  if (d.hd != 64 && d.hd != 96 && d.hd != 128)
+    return fail(LLAMA_ERR_UNSUPPORTED, "head_dim %d not in {64, 96, 128}", d.hd);
+  if (d.D % 64 || d.F % 64) return fail(LLAMA_ERR_UNSUPPORTED, "dim %d / ffn hidden %d not multiples of 64", d.D, d.F);
+  if (d.D > 8192) return fail(LLAMA_ERR_UNSUPPORTED, "dim %d above 8192", d.D);
+  if (d.nrep > 16 || (d.nrep & (d.nrep - 1)))
+    return fail(LLAMA_ERR_UNSUPPORTED, "n_heads/n_kv_heads = %d is not a power of two <= 16", d.nrep);
+  return LLAMA_OK;
+}
+
+// Bump allocator over the caller's workspace; with base == nullptr it only
+// measures.
+struct Carver {
+  char *base;
+  size_t off = 0;
+  explicit Carver(void *b) : base(static_cast<char *>(b)) {}
+  template <typename T>
+  T *take(size_t count) {
+    off = (off + 255) & ~(size_t)255;
+    T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+int ksplit_for(int nblk, int K) {
+  // enough blocks to cover the 256 compute units about 1.5 times, K slices
+  // remaining multiples of 128 (four waves x 32)
+  int ks = 1;
+  while (nblk * ks < 384 && ks < 16 && K % (ks * 2 * 128) == 0) ks *= 2;
+  return ks;
+}
+
+// ------------------------------- prefill layout ------------------------------
+struct PrefillWs {
+  float *h;        // residual stream [T][D] fp32 (llama_prefill only)
+  void *xn;        // [T][D] dtype
+  float2 *tab;     // [S][hd/2]
+  void *q;         // [T][Hq] dtype
+  void *k, *v;     // [B][S][G][hd] dtype (no-cache path)
+  void *o;         // [T][Hq] dtype
+  void *u;         // [T][F] dtype
+  float *qkv;      // fp32 path: [T][Nqkv]
+  float *gate, *up;  // fp32 path: [T][F]
+  // output head (rows = B)
+  u16 *hf;         // bf16: [2][B][D]; fp32 path uses hf32
+  float *hf32;
+  float *logits;   // fp32 path scratch logits [B][V]
+  float *pval;
+  int32_t *pidx;
+  int nblk;
+};
+
+PrefillWs carve_prefill(Carver &c, const Dims &d, int B, int S) {
+  PrefillWs w{};
+  const size_t T = (size_t)B * S;
+  w.h = c.take<float>(T * d.D);
+  w.tab = c.take<float2>((size_t)S * (d.hd / 2));
+  if (d.dt == LLAMA_BF16) {
+    w.xn = c.take<u16>(T * d.D);
+    w.q = c.take<u16>(T * d.Hq());
+    w.k = c.take<u16>(T * d.Hk());
+    w.v = c.take<u16>(T * d.Hk());
+    w.o = c.take<u16>(T * d.Hq());
+    w.u = c.take<u16>(T * d.F);
+  } else {
+    w.xn = c.take<float>(T * d.D);
+    w.qkv = c.take<float>(T * d.Nqkv());
+    w.q = c.take<float>(T * d.Hq());
+    w.k = c.take<float>(T * d.Hk());
+    w.v = c.take<float>(T * d.Hk());
+    w.o = c.take<float>(T * d.Hq());
+    w.gate = c.take<float>(T * d.F);
+    w.up = c.take<float>(T * d.F);
+    w.u = c.take<float>(T * d.F);
+  }
+  return w;
+}
+
+struct HeadWs {
+  u16 *hf;
+  float *hf32;
+  float *logits;
+  float *pval;
+  int32_t *pidx;
+  int nblk;
+};
+
+HeadWs carve_head(Carver &c, const Dims &d, int M) {
+  HeadWs w{};
+  if (d.dt == LLAMA_BF16) {
+    w.hf = c.take<u16>((size_t)2 * M * d.D);
+    w.nblk = skinny_nblk(d.V, SK_LOGITS);
+  } else {
+    w.hf32 = c.take<float>((size_t)M * d.D);
+    w.logits = c.take<float>((size_t)M * d.V);
+    w.nblk = (d.V + 4095) / 4096;
+  }
+  w.pval = c.take<float>((size_t)M * w.nblk);
+  w.pidx = c.take<int32_t>((size_t)M * w.nblk);
+  return w;
+}
+
+// ------------------------------- decode layout -------------------------------
+struct DecodeWs {
+  float *h;         // [B][D]
+  float2 *tab;      // [B][hd/2]
+  void *xn;         // bf16 hi/lo [2][B][D] or fp32 [B][D]
+  float *qkv_part;  // bf16: [ks1][B][Nqkv]; fp32: [B][Nqkv]
+  float *q;         // [B][Hq]
+  float *pm, *pl, *po;
+  void *o;          // bf16 hi/lo [2][B][Hq] or fp32 [B][Hq]
+  float *wo_part;   // [ks2][B][D]
+  void *u;          // bf16 hi/lo [2][B][F] or fp32 [B][F]
+  float *w2_part;   // [ks3][B][D]
+  float *gate, *up; // fp32 path
+  int ks1, ks2, ks3, nchunk;
+};
+
+DecodeWs carve_decode(Carver &c, const Dims &d, int B, int cap) {
+  DecodeWs w{};
+  w.ks1 = ksplit_for(skinny_nblk(d.Nqkv(), SK_PARTIAL), d.D);
+  w.ks2 = ksplit_for(skinny_nblk(d.D, SK_PARTIAL), d.Hq());
+  w.ks3 = ksplit_for(skinny_nblk(d.D, SK_PARTIAL), d.F);
+  w.nchunk = (cap + kDecodeChunk - 1) / kDecodeChunk;
+  const size_t Bz = (size_t)B;
+  w.h = c.take<float>(Bz * d.D);
+  w.tab = c.take<float2>(Bz * (d.hd / 2));
+  w.q = c.take<float>(Bz * d.Hq());
+  w.pm = c.take<float>(Bz * d.H * w.nchunk);
+  w.pl = c.take<float>(Bz * d.H * w.nchunk);
+  w.po = c.take<float>(Bz * d.H * w.nchunk * d.hd);
+  if (d.dt == LLAMA_BF16) {
+    w.xn = c.take<u16>(2 * Bz * d.D);
+    w.qkv_part = c.take<float>((size_t)w.ks1 * Bz * d.Nqkv());
+    w.o = c.take<u16>(2 * Bz * d.Hq());
+    w.wo_part = c.take<float>((size_t)w.ks2 * Bz * d.D);
+    w.u = c.take<u16>(2 * Bz * d.F);
+    w.w2_part = c.take<float>((size_t)w.ks3 * Bz * d.D);
+  } else {
+    w.xn = c.take<float>(Bz * d.D);
+    w.qkv_part = c.take<float>(Bz * d.Nqkv());
+    w.o = c.take<float>(Bz * d.Hq());
+    w.gate = c.take<float>(Bz * d.F);
+    w.up = c.take<float>(Bz * d.F);
+    w.u = c.take<float>(Bz * d.F);
+  }
+  return w;
+}
+
+size_t prefill_bytes(const Dims &d, int B, int S) {
+  Carver c(nullptr);
+  carve_prefill(c, d, B, S);
+  carve_head(c, d, B);
+  return c.off;
+}
+size_t decode_bytes(const Dims &d, int B, int cap) {
+  Carver c(nullptr);
+  carve_decode(c, d, B, cap);
+  carve_head(c, d, B);
+  return c.off;
+}
+
+// ------------------------------- building blocks -----------------------------
+int rmsnorm(const Dims &d, int mode, float *h, int64_t in_off, int64_t in_stride, const float *part, int nsplit,
+            int64_t part_stride, const void *w, float eps, void *out, int64_t out_plane, int rows, hipStream_t s) {
+  NormArgs na{};
+  na.h = h;
+  na.in_offset = in_off;
+  na.in_stride = in_stride;
+  na.part = part;
+  na.nsplit = nsplit;
+  na.part_stride = part_stride;
+  na.w = w;
+  na.eps = eps;
+  na.D = d.D;
+  na.out = out;
+  na.out_plane = out_plane;
+  HIPCHK(launch_rmsnorm(d.dt, mode, na, rows, s));
+  return LLAMA_OK;
+}
+
+// Final head on M rows already normalised into ws (hi/lo planes or fp32).
+int run_head(const Dims &d, const HeadWs &hw, const void *w_out, int M, float *logits, int32_t *ids, hipStream_t s) {
+  if (d.dt == LLAMA_BF16) {
+    for (int r0 = 0; r0 < M; r0 += kSkinnyRows) {
+      const int m = std::min(kSkinnyRows, M - r0);
+      SkinnyArgs sa{};
+      sa.A = hw.hf + (int64_t)r0 * d.D;
+      sa.a_plane = (int64_t)M * d.D;
+      sa.lda = d.D;
+      sa.use_lo = 1;
+      sa.B0 = static_cast<const u16 *>(w_out);
+      sa.M = m;
+      sa.N = d.V;
+      sa.K = d.D;
+      sa.ksplit = 1;
+      sa.logits = logits ? logits + (int64_t)r0 * d.V : nullptr;
+      sa.pval = hw.pval + (int64_t)r0 * hw.nblk;
+      sa.pidx = hw.pidx + (int64_t)r0 * hw.nblk;
+      sa.nblk = hw.nblk;
+      HIPCHK(launch_skinny(SK_LOGITS, sa, s));
+    }
+  } else {
+    float *lg = logits ? logits : hw.logits;
+    HIPCHK(launch_gemm_f32(EPI_STORE_F32, hw.hf32, static_cast<const float *>(w_out), lg, d.V, nullptr, 0, M, d.V, d.D,
+                           s));
+    HIPCHK(launch_argmax_partial(lg, M, d.V, 4096, hw.pval, hw.pidx, hw.nblk, s));
+  }
+  HIPCHK(launch_argmax_reduce(hw.pval, hw.pidx, M, hw.nblk, ids, s));
+  return LLAMA_OK;
+}
+
+// One prefill layer.  h [T][D] fp32 is updated in place (h == y after the
+// copy-free residual epilogues); x_in is the layer input (may equal h).
+int run_layer_prefill(const llama_args *a, const Dims &d, const llama_layer_w *lw, const float *x_in, float *h,
+                      int B, int S, int start_pos, const llama_kv *kv, const PrefillWs &w, bool table_ready,
+                      hipStream_t s) {
+  const int T = B * S;
+  const int cap = kv ? a->max_seq_len : S;
+  void *kc = kv ? kv->k : w.k;
+  void *vc = kv ? kv->v : w.v;
+  if (!table_ready) HIPCHK(launch_rope_table(w.tab, nullptr, start_pos, INT32_MAX, S, d.hd, a->rope_theta, s));
+
+  if (d.dt == LLAMA_BF16) {
+    // a2: attention_norm -> bf16
+    if (int e = rmsnorm(d, 1, const_cast<float *>(x_in), 0, d.D, nullptr, 0, 0, lw->attention_norm, a->norm_eps,
+                        w.xn, 0, T, s))
+      return e;
+    // a3-a5: fused QKV projection + RoPE + K/V write
+    GemmArgs g{};
+    g.A = static_cast<const u16 *>(w.xn);
+    g.lda = d.D;
+    g.B0 = static_cast<const u16 *>(lw->wq);
+    g.B1 = static_cast<const u16 *>(lw->wk);
+    g.B2 = static_cast<const u16 *>(lw->wv);
+    g.ldb = d.D;
+    g.nq = d.Hq();
+    g.nk = d.Hk();
+    g.M = T;
+    g.N = d.Nqkv();
+    g.K = d.D;
+    g.S = S;
+    g.H = d.H;
+    g.G = d.G;
+    g.hd = d.hd;
+    g.start_pos = start_pos;
+    g.cap = cap;
+    g.tab = w.tab;
+    g.q = static_cast<u16 *>(w.q);
+    g.kc = kc;
+    g.vc = vc;
+    HIPCHK(launch_gemm_bf16(EPI_QKV_ROPE, g, s));
+  } else {
+    if (int e = rmsnorm(d, 0, const_cast<float *>(x_in), 0, d.D, nullptr, 0, 0, lw->attention_norm, a->norm_eps,
+                        w.xn, 0, T, s))
+      return e;
+    const float *xn = static_cast<const float *>(w.xn);
+    HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wq), w.qkv, d.Nqkv(), nullptr, 0, T,
+                           d.Hq(), d.D, s));
+    HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wk), w.qkv + d.Hq(), d.Nqkv(), nullptr,
+                           0, T, d.Hk(), d.D, s));
+    HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wv), w.qkv + d.Hq() + d.Hk(), d.Nqkv(),
+                           nullptr, 0, T, d.Hk(), d.D, s));
+    RopeQkvArgs ra{};
+    ra.part = w.qkv;
+    ra.nsplit = 1;
+    ra.part_stride = 0;
+    ra.rows = T;
+    ra.S = S;
+    ra.H = d.H;
+    ra.G = d.G;
+    ra.hd = d.hd;
+    ra.tab = w.tab;
+    ra.tab_mod = S;
+    ra.pos = nullptr;
+    ra.start_pos = start_pos;
+    ra.cap = cap;
+    ra.qout = static_cast<float *>(w.q);
+    ra.kc = kc;
+    ra.vc = vc;
+    HIPCHK(launch_rope_qkv(d.dt, ra, s));
+  }
+  // a6: causal GQA attention
+  AttnArgs at{};
+  at.q = w.q;
+  at.q_stride = d.Hq();
+  at.k = kc;
+  at.v = vc;
+  at.kcap = cap;
+  at.o = w.o;
+  at.B = B;
+  at.S = S;
+  at.H = d.H;
+  at.G = d.G;
+  at.hd = d.hd;
+  at.start_pos = start_pos;
+  at.scale = (float)(1.0 / sqrt((double)d.hd));
+  HIPCHK(launch_attn_prefill(d.dt, at, s));
+
+  if (d.dt == LLAMA_BF16) {
+    // a8: h = x + o wo^T
+    GemmArgs g{};
+    g.A = static_cast<const u16 *>(w.o);
+    g.lda = d.Hq();
+    g.B0 = static_cast<const u16 *>(lw->wo);
+    g.ldb = d.Hq();
+    g.M = T;
+    g.N = d.D;
+    g.K = d.Hq();
+    g.C = h;
+    g.ldc = d.D;
+    g.R = x_in;
+    g.ldr = d.D;
+    HIPCHK(launch_gemm_bf16(EPI_RESID, g, s));
+    // a2: ffn_norm
+    if (int e = rmsnorm(d, 1, h, 0, d.D, nullptr, 0, 0, lw->ffn_norm, a->norm_eps, w.xn, 0, T, s)) return e;
+    // a9: u = silu(xn2 w1^T) * (xn2 w3^T)
+    GemmArgs f{};
+    f.A = static_cast<const u16 *>(w.xn);
+    f.lda = d.D;
+    f.B0 = static_cast<const u16 *>(lw->w1);
+    f.B1 = static_cast<const u16 *>(lw->w3);
+    f.ldb = d.D;
+    f.M = T;
+    f.N = 2 * d.F;
+    f.K = d.D;
+    f.C = w.u;
+    f.ldc = d.F;
+    HIPCHK(launch_gemm_bf16(EPI_SWIGLU, f, s));
+    // a10: h += u w2^T
+    GemmArgs g2{};
+    g2.A = static_cast<const u16 *>(w.u);
+    g2.lda = d.F;
+    g2.B0 = static_cast<const u16 *>(lw->w2);
+    g2.ldb = d.F;
+    g2.M = T;
+    g2.N = d.D;
+    g2.K = d.F;
+    g2.C = h;
+    g2.ldc = d.D;
+    g2.R = h;
+    g2.ldr = d.D;
+    HIPCHK(launch_gemm_bf16(EPI_RESID, g2, s));
+  } else {
+    HIPCHK(launch_gemm_f32(EPI_RESID, static_cast<const float *>(w.o), static_cast<const float *>(lw->wo), h, d.D,
+                           x_in, d.D, T, d.D, d.Hq(), s));
+    if (int e = rmsnorm(d, 0, h, 0, d.D, nullptr, 0, 0, lw->ffn_norm, a->norm_eps, w.xn, 0, T, s)) return e;
+    const float *xn = static_cast<const float *>(w.xn);
+    HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->w1), w.gate, d.F, nullptr, 0, T, d.F, d.D,
+                           s));
+    HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->w3), w.up, d.F, nullptr, 0, T, d.F, d.D,
+                           s));
+    HIPCHK(launch_swiglu(w.gate, w.up, static_cast<float *>(w.u), (int64_t)T * d.F, s));
+    HIPCHK(launch_gemm_f32(EPI_RESID, static_cast<const float *>(w.u), static_cast<const float *>(lw->w2), h, d.D, h,
+                           d.D, T, d.D, d.F, s));
+  }
+  return LLAMA_OK;
+}
+
+int check_layer_w(const llama_layer_w *lw) {
+  if (!lw || !lw->attention_norm || !lw->wq || !lw->wk || !lw->wv || !lw->wo || !lw->ffn_norm || !lw->w1 || !lw->w2 ||
+      !lw->w3)
+    return fail(LLAMA_ERR_ARG, "layer weight pointer is NULL");
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t llama_ffn_hidden_dim(const llama_args *a) {
+  if (!a || a->dim <= 0 || a->multiple_of <= 0) return fail(LLAMA_ERR_ARG, "invalid llama_args");
+  const int32_t f = ffn_hidden(a);
+  return f > 0 ? f : fail(LLAMA_ERR_ARG, "ffn hidden size overflows");
+}
+
+size_t llama_workspace_bytes(const llama_args *a, int32_t batch, int32_t seq_len) {
+  Dims d;
+  if (check_model(a, d) != LLAMA_OK || batch < 1 || seq_len < 1) return 0;
+  const int cap = std::max(a->max_seq_len, 1);
+  return std::max(prefill_bytes(d, batch, seq_len), decode_bytes(d, batch, cap)) + 256;
+}
+
+int llama_layer_forward(const llama_args *a, const llama_layer_w *w, const float *x, float *y, int32_t batch,
+                        int32_t seq_len, int32_t start_pos, const llama_kv *kv, void *ws, size_t ws_bytes,
+                        void *stream) {
+  Dims d;
+  if (int e = check_model(a, d)) return e;
+  if (int e = check_layer_w(w)) return e;
+  if (!x || !y || !ws) return fail(LLAMA_ERR_ARG, "x, y or ws is NULL");
+  if (batch < 1 || seq_len < 1) return fail(LLAMA_ERR_ARG, "batch and seq_len must be >= 1");
+  if (start_pos < 0) return fail(LLAMA_ERR_ARG, "start_pos < 0");
+  if (!kv && start_pos != 0) return fail(LLAMA_ERR_ARG, "start_pos > 0 needs a KV cache");
+  if (kv) {
+    if (!kv->k || !kv->v) return fail(LLAMA_ERR_ARG, "kv->k or kv->v is NULL");
+    if (batch > a->max_batch_size) return fail(LLAMA_ERR_SHAPE, "batch %d > max_batch_size %d", batch, a->max_batch_size);
+    if ((int64_t)start_pos + seq_len > a->max_seq_len)
+      return fail(LLAMA_ERR_SHAPE, "start_pos + seq_len = %lld > max_seq_len %d", (long long)start_pos + seq_len,
+                  a->max_seq_len);
+  }
+  const size_t need = prefill_bytes(d, batch, seq_len);
+  if (ws_bytes < need) return fail(LLAMA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((uintptr_t)ws % 256) return fail(LLAMA_ERR_ARG, "workspace not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  PrefillWs pw = carve_prefill(c, d, batch, seq_len);
+  return run_layer_prefill(a, d, w, x, y, batch, seq_len, start_pos, kv, pw, false, s);
+}
+
+int llama_prefill(const llama_args *a, const llama_model_w *w, const int32_t *ids, int32_t batch, int32_t seq_len,
+                  const llama_kv *kv, float *hidden, float *logits, int32_t *next_id, void *ws, size_t ws_bytes,
+                  void *stream) {
+  Dims d;
+  if (int e = check_model(a, d)) return e;
+  if (!w || !w->tok_embeddings || !w->norm || !w->output || (d.L > 0 && !w->layers))
+    return fail(LLAMA_ERR_ARG, "model weight pointer is NULL");
+  for (int l = 0; l < d.L; ++l)
+    if (int e = check_layer_w(&w->layers[l])) return e;
+  if (!ids || !next_id || !ws) return fail(LLAMA_ERR_ARG, "ids, next_id or ws is NULL");
+  if (batch < 1 || seq_len < 1) return fail(LLAMA_ERR_ARG, "batch and seq_len must be >= 1");
+  if (batch > kSkinnyRows * 1024) return fail(LLAMA_ERR_UNSUPPORTED, "batch %d too large", batch);
+  if (kv) {
+    for (int l = 0; l < d.L; ++l)
+      if (!kv[l].k || !kv[l].v) return fail(LLAMA_ERR_ARG, "kv[%d] has a NULL pointer", l);
+    if (batch > a->max_batch_size) return fail(LLAMA_ERR_SHAPE, "batch %d > max_batch_size %d", batch, a->max_batch_size);
+    if (seq_len > a->max_seq_len) return fail(LLAMA_ERR_SHAPE, "seq_len %d > max_seq_len %d", seq_len, a->max_seq_len);
+  }
+  const size_t need = prefill_bytes(d, batch, seq_len);
+  if (ws_bytes < need) return fail(LLAMA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((uintptr_t)ws % 256) return fail(LLAMA_ERR_ARG, "workspace not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  PrefillWs pw = carve_prefill(c, d, batch, seq_len);
+  HeadWs hw = carve_head(c, d, batch);
+  float *h = hidden ? hidden : pw.h;
+  const int T = batch * seq_len;
+  // a1: embedding rows
+  HIPCHK(launch_embed(d.dt, ids, w->tok_embeddings, h, T, d.D, d.V, s));
+  HIPCHK(launch_rope_table(pw.tab, nullptr, 0, INT32_MAX, seq_len, d.hd, a->rope_theta, s));
+  // a2-a11: layers
+  for (int l = 0; l < d.L; ++l) {
+    if (int e = run_layer_prefill(a, d, &w->layers[l], h, h, batch, seq_len, 0, kv ? &kv[l] : nullptr, pw, true, s))
+      return e;
+  }
+  // a12: final norm of each sequence's last row -> hi/lo (bf16) or fp32
+  if (d.dt == LLAMA_BF16) {
+    if (int e = rmsnorm(d, 2, h, (int64_t)(seq_len - 1) * d.D, (int64_t)seq_len * d.D, nullptr, 0, 0, w->norm,
+                        a->norm_eps, hw.hf, (int64_t)batch * d.D, batch, s))
+      return e;
+  } else {
+    if (int e = rmsnorm(d, 0, h, (int64_t)(seq_len - 1) * d.D, (int64_t)seq_len * d.D, nullptr, 0, 0, w->norm,
+                        a->norm_eps, hw.hf32, 0, batch, s))
+      return e;
+  }
+  // a13-a14: LM head + argmax
+  return run_head(d, hw, w->output, batch, logits, next_id, s);
+}
+
+int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *pos,
+                      int32_t batch, const llama_kv *kv, float *logits, int32_t *next_id, void *ws, size_t ws_bytes,
+                      void *stream) {
+  Dims d;
+  if (int e = check_model(a, d)) return e;
+  if (!w || !w->tok_embeddings || !w->norm || !w->output || (d.L > 0 && !w->layers))
+    return fail(LLAMA_ERR_ARG, "model weight pointer is NULL");
+  for (int l = 0; l < d.L; ++l)
+    if (int e = check_layer_w(&w->layers[l])) return e;
+  if (!ids || !pos || !next_id || !ws || (d.L > 0 && !kv)) return fail(LLAMA_ERR_ARG, "ids, pos, kv, next_id or ws is NULL");
+  for (int l = 0; l < d.L; ++l)
+    if (!kv[l].k || !kv[l].v) return fail(LLAMA_ERR_ARG, "kv[%d] has a NULL pointer", l);
+  if (batch < 1) return fail(LLAMA_ERR_ARG, "batch must be >= 1");
+  if (batch > a->max_batch_size) return fail(LLAMA_ERR_SHAPE, "batch %d > max_batch_size %d", batch, a->max_batch_size);
+  if (a->max_seq_len < 1) return fail(LLAMA_ERR_SHAPE, "max_seq_len < 1");
+  if (d.dt == LLAMA_BF16 && batch > kSkinnyRows)
+    return fail(LLAMA_ERR_UNSUPPORTED, "decode batch %d above %d rows", batch, kSkinnyRows);
+  const int cap = a->max_seq_len;
+  const size_t need = decode_bytes(d, batch, cap);
+  if (ws_bytes < need) return fail(LLAMA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((uintptr_t)ws % 256) return fail(LLAMA_ERR_ARG, "workspace not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  DecodeWs dw = carve_decode(c, d, batch, cap);
+  HeadWs hw = carve_head(c, d, batch);
+  const int B = batch;
+  const bool bf = d.dt == LLAMA_BF16;
+
+  HIPCHK(launch_embed(d.dt, ids, w->tok_embeddings, dw.h, B, d.D, d.V, s));
+  HIPCHK(launch_rope_table(dw.tab, pos, 0, cap - 1, B, d.hd, a->rope_theta, s));
+  const float *pend = nullptr;  // w2 partials of the previous layer still to fold into h
+  int pend_n = 0;
+  for (int l = 0; l < d.L; ++l) {
+    const llama_layer_w *lw = &w->layers[l];
+    // a2 (+ previous layer's a10 residual)
+    if (int e = rmsnorm(d, bf ? 2 : 0, dw.h, 0, d.D, pend, pend_n, (int64_t)B * d.D, lw->attention_norm, a->norm_eps,
+                        dw.xn, (int64_t)B * d.D, B, s))
+      return e;
+    // a3: QKV
+    if (bf) {
+      SkinnyArgs sa{};
+      sa.A = static_cast<const u16 *>(dw.xn);
+      sa.a_plane = (int64_t)B * d.D;
+      sa.lda = d.D;
+      sa.use_lo = 1;
+      sa.B0 = static_cast<const u16 *>(lw->wq);
+      sa.B1 = static_cast<const u16 *>(lw->wk);
+      sa.B2 = static_cast<const u16 *>(lw->wv);
+      sa.nq = d.Hq();
+      sa.nk = d.Hk();
+      sa.M = B;
+      sa.N = d.Nqkv();
+      sa.K = d.D;
+      sa.ksplit = dw.ks1;
+      sa.C = dw.qkv_part;
+      sa.c_plane = (int64_t)B * d.Nqkv();
+      HIPCHK(launch_skinny(SK_PARTIAL, sa, s));
+    } else {
+      const float *xn = static_cast<const float *>(dw.xn);
+      HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wq), dw.qkv_part, d.Nqkv(), nullptr, 0,
+                             B, d.Hq(), d.D, s));
+      HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wk), dw.qkv_part + d.Hq(), d.Nqkv(),
+                             nullptr, 0, B, d.Hk(), d.D, s));
+      HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wv), dw.qkv_part + d.Hq() + d.Hk(),
+                             d.Nqkv(), nullptr, 0, B, d.Hk(), d.D, s));
+    }
+    // a4-a5: RoPE + cache write at pos[b]
+    RopeQkvArgs ra{};
+    ra.part = dw.qkv_part;
+    ra.nsplit = bf ? dw.ks1 : 1;
+    ra.part_stride = (int64_t)B * d.Nqkv();
+    ra.rows = B;
+    ra.S = 1;
+    ra.H = d.H;
+    ra.G = d.G;
+    ra.hd = d.hd;
+    ra.tab = dw.tab;
+    ra.tab_mod = 0;
+    ra.pos = pos;
+    ra.start_pos = 0;
+    ra.cap = cap;
+    ra.qout = dw.q;
+    ra.kc = kv[l].k;
+    ra.vc = kv[l].v;
+    HIPCHK(launch_rope_qkv(d.dt, ra, s));
+    // a7: attention over the cache
+    DecodeAttnArgs da{};
+    da.q = dw.q;
+    da.k = kv[l].k;
+    da.v = kv[l].v;
+    da.pos = pos;
+    da.cap = cap;
+    da.B = B;
+    da.H = d.H;
+    da.G = d.G;
+    da.hd = d.hd;
+    da.chunk = kDecodeChunk;
+    da.nchunk = dw.nchunk;
+    da.scale = (float)(1.0 / sqrt((double)d.hd));
+    da.pm = dw.pm;
+    da.pl = dw.pl;
+    da.po = dw.po;
+    da.out = dw.o;
+    da.out_mode = bf ? 2 : 0;
+    da.out_plane = (int64_t)B * d.Hq();
+    HIPCHK(launch_attn_decode(d.dt, da, s));
+    if (bf) {
+      // a8: wo partials, folded into h by the ffn_norm kernel
+      SkinnyArgs sa{};
+      sa.A = static_cast<const u16 *>(dw.o);
+      sa.a_plane = (int64_t)B * d.Hq();
+      sa.lda = d.Hq();
+      sa.use_lo = 1;
+      sa.B0 = static_cast<const u16 *>(lw->wo);
+      sa.M = B;
+      sa.N = d.D;
+      sa.K = d.Hq();
+      sa.ksplit = dw.ks2;
+      sa.C = dw.wo_part;
+      sa.c_plane = (int64_t)B * d.D;
+      HIPCHK(launch_skinny(SK_PARTIAL, sa, s));
+      if (int e = rmsnorm(d, 2, dw.h, 0, d.D, dw.wo_part, dw.ks2, (int64_t)B * d.D, lw->ffn_norm, a->norm_eps, dw.xn,
+                          (int64_t)B * d.D, B, s))
+        return e;
+      // a9: SwiGLU
+      SkinnyArgs fa{};
+      fa.A = static_cast<const u16 *>(dw.xn);
+      fa.a_plane = (int64_t)B * d.D;
+      fa.lda = d.D;
+      fa.use_lo = 1;
+      fa.B0 = static_cast<const u16 *>(lw->w1);
+      fa.B1 = static_cast<const u16 *>(lw->w3);
+      fa.M = B;
+      fa.N = 2 * d.F;
+      fa.K = d.D;
+      fa.ksplit = 1;
+      fa.C = dw.u;
+      fa.c_plane = (int64_t)B * d.F;
+      HIPCHK(launch_skinny(SK_SWIGLU_HILO, fa, s));
+      // a10: w2 partials (folded by the next norm)
+      SkinnyArgs sb{};
+      sb.A = static_cast<const u16 *>(dw.u);
+      sb.a_plane = (int64_t)B * d.F;
+      sb.lda = d.F;
+      sb.use_lo = 1;
+      sb.B0 = static_cast<const u16 *>(lw->w2);
+      sb.M = B;
+      sb.N = d.D;
+      sb.K = d.F;
+      sb.ksplit = dw.ks3;
+      sb.C = dw.w2_part;
+      sb.c_plane = (int64_t)B * d.D;
+      HIPCHK(launch_skinny(SK_PARTIAL, sb, s));
+      pend = dw.w2_part;
+      pend_n = dw.ks3;
+    } else {
+      HIPCHK(launch_gemm_f32(EPI_RESID, static_cast<const float *>(dw.o), static_cast<const float *>(lw->wo), dw.h,
+                             d.D, dw.h, d.D, B, d.D, d.Hq(), s));
+      if (int e = rmsnorm(d, 0, dw.h, 0, d.D, nullptr, 0, 0, lw->ffn_norm, a->norm_eps, dw.xn, 0, B, s)) return e;
+      const float *xn = static_cast<const float *>(dw.xn);
+      HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->w1), dw.gate, d.F, nullptr, 0, B, d.F,
+                             d.D, s));
+      HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->w3), dw.up, d.F, nullptr, 0, B, d.F,
+                             d.D, s));
+      HIPCHK(launch_swiglu(dw.gate, dw.up, static_cast<float *>(dw.u), (int64_t)B * d.F, s));
+      HIPCHK(launch_gemm_f32(EPI_RESID, static_cast<const float *>(dw.u), static_cast<const float *>(lw->w2), dw.h,
+                             d.D, dw.h, d.D, B, d.D, d.F, s));
+    }
+  }
+  // a12: final norm (folding the last w2 partials)
+  if (bf) {
+    if (int e = rmsnorm(d, 2, dw.h, 0, d.D, pend, pend_n, (int64_t)B * d.D, w->norm, a->norm_eps, hw.hf,
+                        (int64_t)B * d.D, B, s))
+      return e;
+  } else {
+    if (int e = rmsnorm(d, 0, dw.h, 0, d.D, nullptr, 0, 0, w->norm, a->norm_eps, hw.hf32, 0, B, s)) return e;
+  }
+  return run_head(d, hw, w->output, B, logits, next_id, s);
+}
+
+int lm_head_argmax(const llama_args *a, const float *h, const void *final_norm_w, const void *w_out, int32_t M,
+                   float *logits, int32_t *argmax, void *ws, size_t ws_bytes, void *stream) {
+  Dims d;
+  if (int e = check_model(a, d)) return e;
+  if (!h || !w_out || !argmax || !ws) return fail(LLAMA_ERR_ARG, "h, w_out, argmax or ws is NULL");
+  if (M < 1) return fail(LLAMA_ERR_ARG, "M must be >= 1");
+  Carver probe(nullptr);
+  carve_head(probe, d, M);
+  if (ws_bytes < probe.off) return fail(LLAMA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, probe.off);
+  if ((uintptr_t)ws % 256) return fail(LLAMA_ERR_ARG, "workspace not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  HeadWs hw = carve_head(c, d, M);
+  if (d.dt == LLAMA_BF16) {
+    if (int e = rmsnorm(d, 2, const_cast<float *>(h), 0, d.D, nullptr, 0, 0, final_norm_w, a->norm_eps, hw.hf,
+                        (int64_t)M * d.D, M, s))
+      return e;
+  } else {
+    if (int e = rmsnorm(d, 0, const_cast<float *>(h), 0, d.D, nullptr, 0, 0, final_norm_w, a->norm_eps, hw.hf32, 0, M,
+                        s))
+      return e;
+  }
+  return run_head(d, hw, w_out, M, logits, argmax, s);
+}
+
+const char *llama_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,387 @@
+// Causal grouped-query attention [P1 6.11-8; P2 3.3-3.4; P4 GQA]:
+//   for query head h of KV group g = h / n_rep, at absolute position p,
+//   O_h = sum_{j <= p} softmax_j(q_h . k_g[j] / sqrt(hd)) v_g[j]
+// Keys are stored after RoPE; masked keys get exactly zero weight.
+//
+// attn_fwd_bf16   prefill, bf16 MFMA (v_mfma_f32_32x32x16_bf16), online
+//                 softmax in fp32.  One block holds 128 query rows: the n_rep
+//                 heads of one KV group times 128/n_rep positions, so every
+//                 K/V tile staged in LDS serves the whole group.  Scores are
+//                 computed transposed, S^T = K Q^T, so a lane owns one query
+//                 and its softmax statistics; the output is accumulated as
+//                 O^T = V^T P^T, which consumes P^T straight from the score
+//                 registers (V is staged transposed in LDS).
+// attn_fwd_f32    prefill for the fp32 configuration (fp32 FMA, one query
+//                 per thread).
+// attn_decode     one query per sequence over the KV cache, split into key
+//                 chunks (partial max / sum / output), then combined.
+#include "common.h"
+#include "kernels.h"
+
+namespace llk {
+
+namespace {
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Prefill, bf16, MFMA
+// ---------------------------------------------------------------------------
+template <int HD>
+__global__ __launch_bounds__(256) void attn_fwd_bf16(AttnArgs a) {
+  constexpr int KT = 64;          // keys per tile
+  constexpr int KLD = HD + 8;     // K tile row stride (bf16)
+  constexpr int VLD = KT + 8;     // V^T row stride (bf16)
+  constexpr int NT = HD / 16;     // MFMA k-steps over head_dim
+  constexpr int NO = HD / 32;     // output blocks over head_dim
+  __shared__ __align__(16) u16 Ks[KT * KLD];
+  __shared__ __align__(16) u16 Vt[HD * VLD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_rep = a.H / a.G;
+  const int QB = 128 / n_rep;  // positions per block
+  const int qblk = gridDim.x - 1 - blockIdx.x;  // longest blocks first
+  const int g = blockIdx.y, b = blockIdx.z;
+
+  // this lane's query row (B operand column / output column)
+  const int rho = wave * 32 + (lane & 31);
+  const int r_head = rho / QB;
+  const int s = qblk * QB + rho % QB;
+  const bool valid = s < a.S;
+  const int h = g * n_rep + r_head;
+  const int qp = a.start_pos + (valid ? s : a.S - 1);
+  const int gk = lane >> 5;
+
+  const u16 *Q = static_cast<const u16 *>(a.q);
+  const u16 *qrow = Q + (int64_t)(b * a.S + (valid ? s : a.S - 1)) * a.q_stride + h * HD;
+  bf16x8 qf[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) qf[t] = *reinterpret_cast<const bf16x8 *>(qrow + t * 16 + gk * 8);
+
+  f32x16 o[NO];
+#pragma unroll
+  for (int i = 0; i < NO; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const float c = a.scale * kLog2e;
+
+  const int last_s = min(a.S, (qblk + 1) * QB) - 1;
+  const int kv_end = a.start_pos + last_s + 1;  // keys [0, kv_end)
+  const int ntiles = (kv_end + KT - 1) / KT;
+  const u16 *Kg = static_cast<const u16 *>(a.k) + ((int64_t)b * a.kcap * a.G + g) * HD;
+  const u16 *Vg = static_cast<const u16 *>(a.v) + ((int64_t)b * a.kcap * a.G + g) * HD;
+  const int64_t kstride = (int64_t)a.G * HD;
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int k0 = kt * KT;
+    // stage K (row-major) and V (transposed) for keys k0 .. k0+63
+    for (int cidx = tid; cidx < KT * HD / 8; cidx += 256) {
+      const int key = cidx / (HD / 8), c8 = (cidx % (HD / 8)) * 8;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (k0 + key < kv_end) {
+        kv = *reinterpret_cast<const uint4 *>(Kg + (k0 + key) * kstride + c8);
+        vv = *reinterpret_cast<const uint4 *>(Vg + (k0 + key) * kstride + c8);
+      }
+      *reinterpret_cast<uint4 *>(Ks + key * KLD + c8) = kv;
+      const u16 *ve = reinterpret_cast<const u16 *>(&vv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[(c8 + e) * VLD + key] = ve[e];
+    }
+    __syncthreads();
+
+    // S^T = K Q^T for two 32-key blocks
+    f32x16 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+      const u16 *kr = Ks + (kb * 32 + (lane & 31)) * KLD + gk * 8;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8 *>(kr + t * 16), qf[t], sc[kb],
+                                                         0, 0, 0);
+    }
+    // mask, scale, tile max
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + kb * 32 + 8 * (r / 4) + 4 * gk + (r % 4);
+        float v = sc[kb][r] * c;
+        v = key <= qp ? v : -INFINITY;
+        sc[kb][r] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float m_new = fmaxf(m, tmax);
+    const float alpha = exp2f(m - m_new);  // m == -inf on the first tile: alpha = 0
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f(sc[kb][r] - m_new);
+        sc[kb][r] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 32, kWave);
+    l = l * alpha + rs;
+    m = m_new;
+#pragma unroll
+    for (int i = 0; i < NO; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+
+    // P^T fragments (bf16) for the four 16-key steps
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[kb][t][e] = (__bf16)sc[kb][t * 8 + e];
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int ob = 0; ob < NO; ++ob) {
+      const u16 *vr = Vt + (ob * 32 + (lane & 31)) * VLD + 4 * gk;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int kofs = kb * 32 + t * 16;
+          uint4 av;
+          const uint2 lo = *reinterpret_cast<const uint2 *>(vr + kofs);
+          const uint2 hi = *reinterpret_cast<const uint2 *>(vr + kofs + 8);
+          av.x = lo.x; av.y = lo.y; av.z = hi.x; av.w = hi.y;
+          o[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<bf16x8 *>(&av), pf[kb][t], o[ob], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+  }
+
+  if (valid) {
+    const float inv = 1.0f / l;
+    u16 *orow = static_cast<u16 *>(a.o) + (int64_t)(b * a.S + s) * a.q_stride + h * HD;
+#pragma unroll
+    for (int ob = 0; ob < NO; ++ob)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = ob * 32 + 8 * q4 + 4 * gk;
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(o[ob][q4 * 4 + 0] * inv) | ((uint32_t)f2bf(o[ob][q4 * 4 + 1] * inv) << 16);
+        pk.y = (uint32_t)f2bf(o[ob][q4 * 4 + 2] * inv) | ((uint32_t)f2bf(o[ob][q4 * 4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2 *>(orow + d) = pk;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill, fp32 (one wave per block, one query per lane)
+// ---------------------------------------------------------------------------
+template <int HD>
+__global__ __launch_bounds__(64) void attn_fwd_f32(AttnArgs a) {
+  constexpr int KT = 32;
+  __shared__ float Ks[KT][HD];
+  __shared__ float Vs[KT][HD];
+  const int lane = threadIdx.x;
+  const int qblk = gridDim.x - 1 - blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int n_rep = a.H / a.G;
+  const int g = h / n_rep;
+  const int s = qblk * 64 + lane;
+  const bool valid = s < a.S;
+  const int qp = a.start_pos + (valid ? s : a.S - 1);
+  const float *qrow = static_cast<const float *>(a.q) + (int64_t)(b * a.S + (valid ? s : a.S - 1)) * a.q_stride + h * HD;
+  float q[HD], o[HD];
+#pragma unroll
+  for (int d = 0; d < HD; ++d) { q[d] = qrow[d]; o[d] = 0.f; }
+  float m = -INFINITY, l = 0.f;
+  const int kv_end = a.start_pos + min(a.S, (qblk + 1) * 64);
+  const float *Kg = static_cast<const float *>(a.k) + ((int64_t)b * a.kcap * a.G + g) * HD;
+  const float *Vg = static_cast<const float *>(a.v) + ((int64_t)b * a.kcap * a.G + g) * HD;
+  const int64_t kstride = (int64_t)a.G * HD;
+  for (int k0 = 0; k0 < kv_end; k0 += KT) {
+    for (int i = lane; i < KT * HD; i += 64) {
+      const int key = i / HD, d = i % HD;
+      const bool in = k0 + key < kv_end;
+      Ks[key][d] = in ? Kg[(k0 + key) * kstride + d] : 0.f;
+      Vs[key][d] = in ? Vg[(k0 + key) * kstride + d] : 0.f;
+    }
+    __syncthreads();
+    for (int j = 0; j < KT; ++j) {
+      const int key = k0 + j;
+      if (key > qp) break;
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < HD; ++d) dot = fmaf(q[d], Ks[j][d], dot);
+      const float sc = dot * a.scale;
+      const float m_new = fmaxf(m, sc);
+      const float corr = expf(m - m_new);
+      const float p = expf(sc - m_new);
+      l = l * corr + p;
+#pragma unroll
+      for (int d = 0; d < HD; ++d) o[d] = fmaf(p, Vs[j][d], o[d] * corr);
+      m = m_new;
+    }
+    __syncthreads();
+  }
+  if (valid) {
+    float *orow = static_cast<float *>(a.o) + (int64_t)(b * a.S + s) * a.q_stride + h * HD;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) orow[d] = o[d] * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode: one query per sequence, split over key chunks
+// ---------------------------------------------------------------------------
+template <typename TC, int HD>
+__global__ __launch_bounds__(256) void attn_decode_kernel(DecodeAttnArgs a) {
+  constexpr int MAXREP = 16;
+  constexpr int CH = 256;  // keys per chunk (a.chunk == CH)
+  __shared__ float qs[MAXREP][HD];
+  __shared__ float sc[MAXREP][CH];
+  __shared__ float ml[MAXREP][2];
+  const int tid = threadIdx.x;
+  const int ci = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int n_rep = a.H / a.G;
+  int pb = a.pos[b];
+  pb = pb < 0 ? 0 : (pb > a.cap - 1 ? a.cap - 1 : pb);
+  const int c0 = ci * CH;
+  const int kend = min(c0 + CH, pb + 1);
+  const int64_t pidx = ((int64_t)b * a.H + g * n_rep) * a.nchunk + ci;  // + r * nchunk per head
+  if (c0 >= kend) {
+    for (int i = tid; i < n_rep * HD; i += 256) {
+      const int r = i / HD, d = i % HD;
+      a.po[(pidx + (int64_t)r * a.nchunk) * HD + d] = 0.f;
+    }
+    if (tid < n_rep) {
+      a.pm[pidx + (int64_t)tid * a.nchunk] = -INFINITY;
+      a.pl[pidx + (int64_t)tid * a.nchunk] = 0.f;
+    }
+    return;
+  }
+  const int nk = kend - c0;
+  for (int i = tid; i < n_rep * HD; i += 256) {
+    const int r = i / HD, d = i % HD;
+    qs[r][d] = a.q[((int64_t)b * a.H + g * n_rep + r) * HD + d];
+  }
+  __syncthreads();
+  const TC *Kg = static_cast<const TC *>(a.k) + ((int64_t)b * a.cap * a.G + g) * HD;
+  const TC *Vg = static_cast<const TC *>(a.v) + ((int64_t)b * a.cap * a.G + g) * HD;
+  const int64_t kstride = (int64_t)a.G * HD;
+  if (tid < nk) {
+    const TC *kr = Kg + (int64_t)(c0 + tid) * kstride;
+    float dot[MAXREP];
+    for (int r = 0; r < n_rep; ++r) dot[r] = 0.f;
+    for (int d = 0; d < HD; ++d) {
+      const float kv = Elem<TC>::load(kr + d);
+      for (int r = 0; r < n_rep; ++r) dot[r] = fmaf(qs[r][d], kv, dot[r]);
+    }
+    for (int r = 0; r < n_rep; ++r) sc[r][tid] = dot[r] * a.scale;
+  }
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int r = wave; r < n_rep; r += 4) {
+    float mx = -INFINITY;
+    for (int j = lane; j < nk; j += 64) mx = fmaxf(mx, sc[r][j]);
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int j = lane; j < nk; j += 64) {
+      const float p = expf(sc[r][j] - mx);
+      sc[r][j] = p;
+      sum += p;
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) { ml[r][0] = mx; ml[r][1] = sum; }
+  }
+  __syncthreads();
+  for (int i = tid; i < n_rep * HD; i += 256) {
+    const int r = i / HD, d = i % HD;
+    float acc = 0.f;
+    for (int j = 0; j < nk; ++j) acc = fmaf(sc[r][j], Elem<TC>::load(Vg + (int64_t)(c0 + j) * kstride + d), acc);
+    a.po[(pidx + (int64_t)r * a.nchunk) * HD + d] = acc;
+  }
+  if (tid < n_rep) {
+    a.pm[pidx + (int64_t)tid * a.nchunk] = ml[tid][0];
+    a.pl[pidx + (int64_t)tid * a.nchunk] = ml[tid][1];
+  }
+}
+
+// Combine the chunk partials of one (sequence, head):
+// O = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c, M = max_c m_c.
+template <int HD>
+__global__ __launch_bounds__(HD) void attn_combine_kernel(DecodeAttnArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int64_t base = ((int64_t)b * a.H + h) * a.nchunk;
+  float M = -INFINITY;
+  for (int c = 0; c < a.nchunk; ++c) M = fmaxf(M, a.pm[base + c]);
+  float L = 0.f, acc = 0.f;
+  for (int c = 0; c < a.nchunk; ++c) {
+    const float mc = a.pm[base + c];
+    if (mc == -INFINITY) continue;
+    const float w = expf(mc - M);
+    L += w * a.pl[base + c];
+    acc += w * a.po[(base + c) * HD + d];
+  }
+  const float v = acc / L;
+  const int64_t o = (int64_t)b * a.H * HD + h * HD + d;
+  if (a.out_mode == 0) {
+    static_cast<float *>(a.out)[o] = v;
+  } else {
+    u16 hi, lo;
+    split_hilo(v, hi, lo);
+    static_cast<u16 *>(a.out)[o] = hi;
+    static_cast<u16 *>(a.out)[a.out_plane + o] = lo;
+  }
+}
+
+template <int HD>
+hipError_t prefill_hd(int dtype, const AttnArgs &a, hipStream_t s) {
+  if (dtype == 1) {
+    const int QB = 128 / (a.H / a.G);
+    dim3 grid((a.S + QB - 1) / QB, a.G, a.B);
+    hipLaunchKernelGGL(attn_fwd_bf16<HD>, grid, dim3(256), 0, s, a);
+  } else {
+    dim3 grid((a.S + 63) / 64, a.H, a.B);
+    hipLaunchKernelGGL(attn_fwd_f32<HD>, grid, dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int HD>
+hipError_t decode_hd(int dtype, const DecodeAttnArgs &a, hipStream_t s) {
+  dim3 grid(a.nchunk, a.G, a.B);
+  if (dtype == 1)
+    hipLaunchKernelGGL((attn_decode_kernel<u16, HD>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<float, HD>), grid, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine_kernel<HD>, dim3(a.H, a.B), dim3(HD), 0, s, a);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attn_prefill(int dtype, const AttnArgs &a, hipStream_t s) {
+  switch (a.hd) {
+    case 64: return prefill_hd<64>(dtype, a, s);
+    case 96: return prefill_hd<96>(dtype, a, s);
+    case 128: return prefill_hd<128>(dtype, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_decode(int dtype, const DecodeAttnArgs &a, hipStream_t s) {
+  switch (a.hd) {
+    case 64: return decode_hd<64>(dtype, a, s);
+    case 96: return decode_hd<96>(dtype, a, s);
+    case 128: return decode_hd<128>(dtype, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace llk

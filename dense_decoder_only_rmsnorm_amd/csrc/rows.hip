@@ -1,0 +1,328 @@
+// Row-wise kernels: embedding gather, RMSNorm (with optional split-K partial
+// accumulation into the residual stream), RoPE table, RoPE + KV-cache write,
+// SwiGLU gate (fp32 path), argmax reduction.
+//
+// Pages: [P1] llama3-from-scratch translation (sections 4, 5, 6.6-6.9, 9.3, 12);
+//        [P2] "Build your own Llama 3" notes (sections 3.1-3.5);
+//        [P3] llama3-from-scratch output layer page (steps 1-4).
+#include "common.h"
+#include "kernels.h"
+
+namespace llk {
+
+// ---------------------------------------------------------------------------
+// Embedding lookup [P1 4; P2 4 tok_embeddings]: h[r, :] = E[ids[r], :] as fp32.
+// Ids outside [0, V) produce NaN rows instead of an out-of-bounds read.
+// One block per row, 8 elements per thread and step.
+// ---------------------------------------------------------------------------
+template <typename TW>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ ids, const TW *__restrict__ E,
+                                                    float *__restrict__ h, int D, int V) {
+  const int r = blockIdx.x;
+  const int id = ids[r];
+  float *dst = h + (int64_t)r * D;
+  const bool ok = id >= 0 && id < V;
+  const TW *src = E + (int64_t)(ok ? id : 0) * D;
+  for (int i = threadIdx.x * 4; i < D; i += 256 * 4) {
+    float4 v;
+    if (ok) {
+      v = make_float4(Elem<TW>::load(src + i), Elem<TW>::load(src + i + 1), Elem<TW>::load(src + i + 2),
+                      Elem<TW>::load(src + i + 3));
+    } else {
+      v = make_float4(__int_as_float(0x7fc00000), __int_as_float(0x7fc00000), __int_as_float(0x7fc00000),
+                      __int_as_float(0x7fc00000));
+    }
+    *reinterpret_cast<float4 *>(dst + i) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm [P1 5; P2 3.1; P3 step 1]: y = x / sqrt(mean(x^2) + eps) * w, with
+// the mean over the model dimension, eps inside the root and the weight
+// applied after normalising.  fp32 arithmetic, one rounding at the store.
+//
+// Optionally first folds split-K partial sums into the residual stream:
+//   x[r] += sum_s part[s][r]   (written back to x).
+// w == nullptr skips the normalisation (pure conversion of x).
+// Output modes: 0 fp32, 1 bf16, 2 bf16 hi/lo planes (hi at out, lo at
+// out + out_plane).  One block of 256 threads per row; D <= 8192.
+// ---------------------------------------------------------------------------
+template <typename TW, int MODE>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
+  constexpr int MAXV = 8;
+  const int r = blockIdx.x;
+  const int D = a.D;
+  float *x = a.h + a.in_offset + (int64_t)r * a.in_stride;
+  float4 v[MAXV];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int i = (j * 256 + threadIdx.x) * 4;
+    if (i < D) {
+      float4 t = *reinterpret_cast<const float4 *>(x + i);
+      if (a.nsplit > 0) {
+        for (int s = 0; s < a.nsplit; ++s) {
+          const float4 p = *reinterpret_cast<const float4 *>(a.part + s * a.part_stride + (int64_t)r * D + i);
+          t.x += p.x; t.y += p.y; t.z += p.z; t.w += p.w;
+        }
+        *reinterpret_cast<float4 *>(x + i) = t;
+      }
+      v[j] = t;
+      ss += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
+    }
+  }
+  float scale = 1.f;
+  if (a.w != nullptr) {
+    __shared__ float red[4];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    scale = 1.0f / sqrtf(tot / (float)D + a.eps);
+  }
+  const TW *w = static_cast<const TW *>(a.w);
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int i = (j * 256 + threadIdx.x) * 4;
+    if (i < D) {
+      float y[4] = {v[j].x * scale, v[j].y * scale, v[j].z * scale, v[j].w * scale};
+      if (w != nullptr) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] *= Elem<TW>::load(w + i + e);
+      }
+      const int64_t o = (int64_t)r * D + i;
+      if (MODE == 0) {
+        *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + o) = make_float4(y[0], y[1], y[2], y[3]);
+      } else if (MODE == 1) {
+        u16 *p = static_cast<u16 *>(a.out) + o;
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(y[0]) | ((uint32_t)f2bf(y[1]) << 16);
+        pk.y = (uint32_t)f2bf(y[2]) | ((uint32_t)f2bf(y[3]) << 16);
+        *reinterpret_cast<uint2 *>(p) = pk;
+      } else {
+        u16 hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_hilo(y[e], hi[e], lo[e]);
+        u16 *p = static_cast<u16 *>(a.out) + o;
+        uint2 ph, pl;
+        ph.x = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
+        ph.y = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
+        pl.x = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+        pl.y = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
+        *reinterpret_cast<uint2 *>(p) = ph;
+        *reinterpret_cast<uint2 *>(p + a.out_plane) = pl;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RoPE table [P2 3.2 precompute_freqs_cis; P1 6.7]: for table row r at
+// position p_r and pair i < hd/2, tab[r][i] = (cos, sin)(p_r * theta_i) with
+// theta_i = rope_theta^(-2i/hd).  The angle and its cosine/sine are evaluated
+// in fp64 and rounded once to fp32, so large positions keep full accuracy.
+// p_r = pos[r] (clamped to [0, pos_max]) when pos != nullptr, else
+// start_pos + r.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rope_table_kernel(float2 *__restrict__ tab, const int32_t *__restrict__ pos,
+                                                         int start_pos, int pos_max, int rows, int half,
+                                                         double log2_theta) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * half) return;
+  const int r = idx / half, i = idx % half;
+  int p = pos ? pos[r] : start_pos + r;
+  p = p < 0 ? 0 : (p > pos_max ? pos_max : p);
+  const double inv_freq = exp2(-(2.0 * i / (2.0 * half)) * log2_theta);
+  double s, c;
+  sincos((double)p * inv_freq, &s, &c);
+  tab[idx] = make_float2((float)c, (float)s);
+}
+
+// ---------------------------------------------------------------------------
+// RoPE + KV-cache write for Q/K/V rows held in fp32 (split-K partials summed
+// first) [P2 3.2 apply_rotary_emb, 3.3-3.4 cache write; P1 6.8-6.10].
+//   qkv row r = [q (H*hd) | k (G*hd) | v (G*hd)], sum over nsplit partials.
+//   q, k: adjacent pairs rotated by the table row of r; v copied.
+//   q -> qout[r][H*hd] (fp32); k, v -> cache[b][p][g][hd] (TC), where
+//   b = r / S, s = r % S and p = (pos ? clamp(pos[b]) : start_pos) + s.
+// One thread per pair.
+// ---------------------------------------------------------------------------
+template <typename TC>
+__global__ __launch_bounds__(256) void rope_qkv_kernel(RopeQkvArgs a) {
+  const int npair = (a.H + 2 * a.G) * a.hd / 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)a.rows * npair) return;
+  const int r = (int)(idx / npair);
+  const int j = (int)(idx % npair) * 2;  // even column
+  const int N = (a.H + 2 * a.G) * a.hd;
+  float x0 = 0.f, x1 = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float2 t = *reinterpret_cast<const float2 *>(a.part + s * a.part_stride + (int64_t)r * N + j);
+    x0 += t.x;
+    x1 += t.y;
+  }
+  const int b = r / a.S, sidx = r % a.S;
+  int p0 = a.pos ? a.pos[b] : a.start_pos;
+  p0 = p0 < 0 ? 0 : (p0 > a.cap - 1 ? a.cap - 1 : p0);
+  int p = p0 + sidx;
+  p = p > a.cap - 1 ? a.cap - 1 : p;
+  const int Hq = a.H * a.hd, Hk = a.G * a.hd;
+  const int tr = a.tab_mod > 0 ? (r % a.tab_mod) : r;
+  if (j < Hq + Hk) {
+    const int d = (j < Hq ? j : j - Hq) % a.hd;
+    const float2 cs = a.tab[(int64_t)tr * (a.hd / 2) + d / 2];
+    const float2 y = rotate_pair(x0, x1, cs.x, cs.y);
+    x0 = y.x;
+    x1 = y.y;
+  }
+  if (j < Hq) {
+    *reinterpret_cast<float2 *>(a.qout + (int64_t)r * Hq + j) = make_float2(x0, x1);
+  } else {
+    const bool isk = j < Hq + Hk;
+    const int c = isk ? j - Hq : j - Hq - Hk;
+    const int g = c / a.hd, d = c % a.hd;
+    TC *base = static_cast<TC *>(isk ? a.kc : a.vc);
+    TC *dst = base + (((int64_t)b * a.cap + p) * a.G + g) * a.hd + d;
+    Elem<TC>::store(dst, x0);
+    Elem<TC>::store(dst + 1, x1);
+  }
+}
+
+// SwiGLU gate for the fp32 path [P2 3.5; P1 9.3]: u = silu(gate) * up.
+__global__ __launch_bounds__(256) void swiglu_kernel(const float *__restrict__ gate, const float *__restrict__ up,
+                                                     float *__restrict__ u, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) u[i] = silu(gate[i]) * up[i];
+}
+
+// ---------------------------------------------------------------------------
+// Argmax over per-block partial maxima [P1 12; P3 4]: for each row pick the
+// largest value, and among equal values the smallest index.
+// part_val/part_idx: [rows][nblk].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(256) void argmax_reduce_kernel(const float *__restrict__ part_val,
+                                                            const int32_t *__restrict__ part_idx, int nblk,
+                                                            int32_t *__restrict__ out) {
+  const int r = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int j = threadIdx.x; j < nblk; j += 256) {
+    const float v = part_val[(int64_t)r * nblk + j];
+    const int i = part_idx[(int64_t)r * nblk + j];
+    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float v = __shfl_xor(bv, o, kWave);
+    const int i = __shfl_xor(bi, o, kWave);
+    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
+    out[r] = bi == 0x7fffffff ? 0 : bi;
+  }
+}
+
+// Row-wise argmax of a dense fp32 [rows][n] matrix into per-block partials
+// (fp32 path LM head).  Block (r, j) scans columns [j*chunk, (j+1)*chunk).
+__global__ __launch_bounds__(256) void argmax_partial_kernel(const float *__restrict__ x, int n, int chunk,
+                                                             float *__restrict__ part_val,
+                                                             int32_t *__restrict__ part_idx, int nblk) {
+  const int r = blockIdx.y, j = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  const int c1 = min(n, (j + 1) * chunk);
+  for (int c = j * chunk + threadIdx.x; c < c1; c += 256) {
+    const float v = x[(int64_t)r * n + c];
+    if (better(v, c, bv, bi)) { bv = v; bi = c; }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float v = __shfl_xor(bv, o, kWave);
+    const int i = __shfl_xor(bi, o, kWave);
+    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
+    part_val[(int64_t)r * nblk + j] = bv;
+    part_idx[(int64_t)r * nblk + j] = bi;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_embed(int dtype, const int32_t *ids, const void *E, float *h, int rows, int D, int V,
+                        hipStream_t s) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(rows), dim3(256), 0, s, ids, (const float *)E, h, D, V);
+  else
+    hipLaunchKernelGGL(embed_kernel<u16>, dim3(rows), dim3(256), 0, s, ids, (const u16 *)E, h, D, V);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int dtype, int mode, const NormArgs &a, int rows, hipStream_t s) {
+#define LLK_NORM(TW, M) hipLaunchKernelGGL((rmsnorm_kernel<TW, M>), dim3(rows), dim3(256), 0, s, a)
+  if (dtype == 0) {
+    if (mode == 0) LLK_NORM(float, 0);
+    else if (mode == 1) LLK_NORM(float, 1);
+    else LLK_NORM(float, 2);
+  } else {
+    if (mode == 0) LLK_NORM(u16, 0);
+    else if (mode == 1) LLK_NORM(u16, 1);
+    else LLK_NORM(u16, 2);
+  }
+#undef LLK_NORM
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float2 *tab, const int32_t *pos, int start_pos, int pos_max, int rows, int hd,
+                             double theta, hipStream_t s) {
+  const int n = rows * (hd / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, tab, pos, start_pos, pos_max, rows,
+                     hd / 2, log2(theta));
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_qkv(int dtype, const RopeQkvArgs &a, hipStream_t s) {
+  const int64_t n = (int64_t)a.rows * ((a.H + 2 * a.G) * a.hd / 2);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (dtype == 0)
+    hipLaunchKernelGGL(rope_qkv_kernel<float>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(rope_qkv_kernel<u16>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const float *gate, const float *up, float *u, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gate, up, u, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_reduce(const float *pv, const int32_t *pi, int rows, int nblk, int32_t *out,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(rows), dim3(256), 0, s, pv, pi, nblk, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_partial(const float *x, int rows, int n, int chunk, float *pv, int32_t *pi, int nblk,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL(argmax_partial_kernel, dim3(nblk, rows), dim3(256), 0, s, x, n, chunk, pv, pi, nblk);
+  return hipGetLastError();
+}
+
+}  // namespace llk

@@ -1,0 +1,173 @@
+/*
+ * llama_mi355x.h - C ABI of the MI355X (gfx950) Llama-3 decoder forward pass.
+ *
+ * The library computes the dense decoder-only forward pass described on the
+ * pages cited below: RMSNorm, Q/K/V projections, rotary position embedding
+ * (RoPE), causal grouped-query attention (GQA), output projection, SwiGLU
+ * feed-forward, final RMSNorm, LM-head logits and argmax.
+ *
+ * Pages (cited by title and section):
+ *   [P1] "机器学习 | 从0开发大模型—译llama3-from-scratch" (sunaigc.com translation
+ *        of the llama3-from-scratch notebook)
+ *   [P2] "Build your own Llama 3 architecture from scratch" notes (gitcode.csdn.net)
+ *   [P3] "大语言模型实现llama3-from-scratch：输出层与预测" (agent.csdn.net)
+ *   [P4] joto.ai blog post on the Llama architecture (GQA, RoPE, RMSNorm)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership: the caller owns every buffer (weights, activations, KV cache,
+ *   logits, ids, workspace).  Pointers marked "device" are HIP device
+ *   pointers; the library allocates nothing and keeps no pointer after it
+ *   returns.  All work is enqueued asynchronously on `stream` (a hipStream_t
+ *   passed as void*; NULL is the null stream); outputs are valid once the
+ *   stream has completed.  Nothing synchronises the host.
+ * Layouts: contiguous row-major, device pointers 16-byte aligned.  Linear
+ *   weights are [out, in] as in nn.Linear [P2 3.4, 3.5; P1 6.2].  Head h of
+ *   wq occupies rows [h*hd, (h+1)*hd) [P1 6.3]; wo's input columns are the
+ *   heads concatenated in order [P1 8].
+ * Number types: `dtype` (llama_args.dtype) is the storage type of weights,
+ *   norm weights, embeddings and the KV cache: LLAMA_F32 or LLAMA_BF16.
+ *   Hidden states passed in and out (the residual stream) are always fp32;
+ *   logits are always fp32 [P2 4 `logits.float()`; P3 numerics]; token ids
+ *   are int32.  bf16 contractions accumulate in fp32.
+ * Errors: every entry point returns LLAMA_OK (0) or a negative llama_status.
+ *   Arguments are validated before any HIP call; on error nothing has been
+ *   enqueued and llama_last_error() describes the cause (thread-local).
+ *   LLAMA_ERR_HIP reports a failed launch or runtime call; work enqueued
+ *   before the failure may have run.  Token ids outside [0, vocab) are a
+ *   caller error: their embedding rows are filled with NaN.
+ */
+#ifndef LLAMA_MI355X_H
+#define LLAMA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LLAMA_OK = 0,
+  LLAMA_ERR_ARG = -1,         /* null pointer or invalid scalar argument */
+  LLAMA_ERR_SHAPE = -2,       /* inconsistent shapes (see each function) */
+  LLAMA_ERR_UNSUPPORTED = -3, /* a shape the kernels do not specialise */
+  LLAMA_ERR_WORKSPACE = -4,   /* workspace smaller than llama_workspace_bytes() */
+  LLAMA_ERR_HIP = -5          /* HIP launch or runtime failure */
+} llama_status;
+
+typedef enum { LLAMA_F32 = 0, LLAMA_BF16 = 1 } llama_dtype;
+
+/* Model hyper-parameters; mirrors ModelArgs [P2 1.2] and params.json [P1 2].
+ * ffn_dim_multiplier <= 0 encodes None.  max_batch_size / max_seq_len give
+ * the KV-cache capacity [P2 3.3]. */
+typedef struct {
+  int32_t dim, n_layers, n_heads, n_kv_heads, vocab_size;
+  int32_t multiple_of;
+  float ffn_dim_multiplier;
+  float norm_eps;
+  float rope_theta;
+  int32_t max_batch_size, max_seq_len;
+  int32_t dtype; /* llama_dtype */
+} llama_args;
+
+/* One decoder layer's weights (device, dtype).  Names follow the checkpoint
+ * keys [P1 2]: attention_norm [D], wq [H*hd, D], wk [G*hd, D], wv [G*hd, D],
+ * wo [D, H*hd], ffn_norm [D], w1 [F, D], w2 [D, F], w3 [F, D]. */
+typedef struct {
+  const void *attention_norm, *wq, *wk, *wv, *wo, *ffn_norm, *w1, *w2, *w3;
+} llama_layer_w;
+
+/* Whole model: tok_embeddings [V, D], layers (HOST array of n_layers
+ * llama_layer_w), norm [D], output [V, D]; tensors on the device. */
+typedef struct {
+  const void *tok_embeddings;
+  const llama_layer_w *layers;
+  const void *norm, *output;
+} llama_model_w;
+
+/* One layer's KV cache (device, dtype): k and v each
+ * [max_batch_size][max_seq_len][n_kv_heads][head_dim].  Keys are stored
+ * after RoPE [P2 3.3-3.4]. */
+typedef struct {
+  void *k, *v;
+} llama_kv;
+
+/* SwiGLU hidden size F [P2 3.5]: int(2*(4*dim)/3), times ffn_dim_multiplier
+ * (truncated) when set, rounded up to a multiple of multiple_of.  Returns a
+ * negative llama_status on invalid arguments. */
+int32_t llama_ffn_hidden_dim(const llama_args *a);
+
+/* Bytes of device workspace that llama_layer_forward and llama_prefill need
+ * for (batch, seq_len) and that llama_decode_step and lm_head_argmax need
+ * for `batch` rows.  Returns 0 on invalid arguments.  Pass the workspace as
+ * `ws`, at least 256-byte aligned. */
+size_t llama_workspace_bytes(const llama_args *a, int32_t batch, int32_t seq_len);
+
+/* One pre-norm decoder block [P2 3.6; P1 6-10] on hidden states
+ *   x[batch][seq_len][dim] (fp32, device) at positions start_pos + s:
+ *     h1 = x  + wo( GQA( rope(q), rope(k), v ) ),  q,k,v = rmsnorm(x) W^T
+ *     y  = h1 + w2( silu(w1 xn2) * w3 xn2 ),        xn2  = rmsnorm(h1)
+ * y[batch][seq_len][dim] (fp32, device) may alias x.
+ * kv (nullable): when given, the new keys/values are written to
+ *   kv->k/v[b][start_pos + s] and queries attend to cache positions
+ *   0..start_pos+s (chunked prefill); when NULL, start_pos must be 0 and
+ *   attention runs over the chunk itself [P2 3.4 training branch].
+ * Errors: ERR_ARG (null x/y/w/ws, start_pos < 0, start_pos > 0 without kv),
+ *   ERR_SHAPE (dim % n_heads, n_heads % n_kv_heads, odd head_dim,
+ *   batch > max_batch_size with kv, start_pos + seq_len > max_seq_len [P2 6
+ *   assert]), ERR_UNSUPPORTED (head_dim not in {64, 96, 128}, dim or F not a
+ *   multiple of 64, n_heads/n_kv_heads not a power of two <= 16),
+ *   ERR_WORKSPACE. */
+int llama_layer_forward(const llama_args *a, const llama_layer_w *w, const float *x, float *y,
+                        int32_t batch, int32_t seq_len, int32_t start_pos, const llama_kv *kv,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Prefill of `batch` sequences of `seq_len` tokens from position 0
+ * [P2 4 Transformer.forward; P1 4-12]: embedding lookup, n_layers blocks,
+ * final RMSNorm of each sequence's last position, LM head, argmax.
+ *   ids     [batch][seq_len] int32 (device)
+ *   kv      nullable HOST array of n_layers llama_kv; when given the caches
+ *           are filled at positions 0..seq_len-1
+ *   hidden  nullable; receives the residual stream after the last layer,
+ *           [batch][seq_len][dim] fp32 (device)
+ *   logits  nullable; receives last-position logits [batch][vocab] fp32
+ *   next_id [batch] int32 (device): argmax of each row of the logits, the
+ *           smallest index on ties [P1 12; P3 4]
+ * Errors: as llama_layer_forward, plus ERR_ARG for null ids/next_id. */
+int llama_prefill(const llama_args *a, const llama_model_w *w, const int32_t *ids, int32_t batch,
+                  int32_t seq_len, const llama_kv *kv, float *hidden, float *logits, int32_t *next_id,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* One decode step: one new token per sequence [P2 3.3, 6 generate].
+ *   ids [batch] int32 (device): the new tokens
+ *   pos [batch] int32 (device): each sequence's current cache length; the
+ *       new key/value go to cache slot pos[b] and the token attends to
+ *       positions 0..pos[b] [P2 3.4 inference branch].  Each pos[b] must lie
+ *       in [0, max_seq_len); out-of-range entries are clamped by the kernels
+ *       so no access leaves the cache.
+ *   kv  HOST array of n_layers llama_kv (required)
+ *   logits nullable [batch][vocab] fp32; next_id [batch] int32 (device).
+ * Errors: ERR_ARG (null ids/pos/kv/next_id), ERR_SHAPE (batch >
+ *   max_batch_size), ERR_UNSUPPORTED, ERR_WORKSPACE. */
+int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *pos,
+                      int32_t batch, const llama_kv *kv, float *logits, int32_t *next_id, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* Output head on M hidden rows [P1 11-12; P3 1-4]:
+ *   h [M][dim] fp32 (device); final_norm_w (nullable, dtype) applies the
+ *   final RMSNorm first; w_out [vocab][dim] (dtype).
+ *   logits (nullable) [M][vocab] fp32; argmax [M] int32, smallest index on
+ *   ties.  Errors: ERR_ARG (null h/w_out/argmax, M < 1), ERR_UNSUPPORTED
+ *   (dim not a multiple of 64), ERR_WORKSPACE (needs
+ *   llama_workspace_bytes(a, M, 1)). */
+int lm_head_argmax(const llama_args *a, const float *h, const void *final_norm_w, const void *w_out, int32_t M,
+                   float *logits, int32_t *argmax, void *ws, size_t ws_bytes, void *stream);
+
+/* Message describing the last non-OK return on the calling thread. */
+const char *llama_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLAMA_MI355X_H */

@@ -271,7 +271,7 @@ def prefill(ids, embed_rows: Callable, layer: LayerSource, norm_w, w_out, args: 
     hs = [_f64(embed_rows(ids[b])) for b in range(B)]
     positions = np.arange(S)
     for l in range(args["n_layers"]):
-        lw = layer(l)
+        lw = {k: _f64(v) for k, v in layer(l).items()}  # widen once per layer
         for b in range(B):
             cache = None
             if caches is not None:
@@ -300,7 +300,7 @@ def decode_step(ids, caches: Sequence[Sequence[dict]], embed_rows: Callable, lay
     B = ids.shape[0]
     hs = [_f64(embed_rows(ids[b:b + 1])) for b in range(B)]
     for l in range(args["n_layers"]):
-        lw = layer(l)
+        lw = {k: _f64(v) for k, v in layer(l).items()}  # widen once per layer
         for b in range(B):
             c = caches[b][l]
             p = c["k"].shape[0]

@@ -1,0 +1,127 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+derives the FFN size like the oracle, sizes workspaces, and rejects bad
+arguments before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import dense_decoder_only_rmsnorm_amd as M
+import inputs as I
+from oracle import llama as OL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for f in os.listdir(inc):
+        if not f.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, f)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = M.lib()
+    decl = _declared_symbols()
+    assert set(M.EXPORTED) <= set(decl)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3_s17", "c4", "c5"])
+def test_ffn_hidden_dim_agrees_with_oracle(key):
+    cfg = I.CONFIGS[key]
+    args = M.make_args(cfg.dim, cfg.n_layers, cfg.n_heads, cfg.n_kv_heads, cfg.vocab_size, cfg.multiple_of,
+                       cfg.ffn_dim_multiplier, cfg.norm_eps, cfg.rope_theta)
+    assert M.llama_ffn_hidden_dim(args) == OL.ffn_hidden_dim(cfg.dim, cfg.multiple_of, cfg.ffn_dim_multiplier)
+
+
+def _args(**kw):
+    base = dict(dim=512, n_layers=2, n_heads=8, n_kv_heads=4, vocab_size=68, multiple_of=256,
+                ffn_dim_multiplier=None, norm_eps=1e-5, rope_theta=5e5, max_batch_size=4, max_seq_len=64,
+                dtype=M.LLAMA_BF16)
+    base.update(kw)
+    return M.make_args(**base)
+
+
+def test_workspace_bytes_grows_with_tokens():
+    a = _args()
+    n1 = M.llama_workspace_bytes(a, 1, 16)
+    n2 = M.llama_workspace_bytes(a, 2, 64)
+    assert 0 < n1 < n2
+    with pytest.raises(M.LlamaError):
+        M.llama_workspace_bytes(_args(dim=500), 1, 16)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation returns first
+
+
+def _layer_fake():
+    return M.llama_layer_w(*([0x1000] * 9))
+
+
+def _call_layer(a, x=FAKE, y=FAKE, batch=1, seq=8, start=0, kv=None, ws=FAKE, ws_bytes=1 << 40):
+    return M.lib().llama_layer_forward(ctypes.byref(a), ctypes.byref(_layer_fake()), x, y, batch, seq, start,
+                                       kv, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dim=510, n_heads=6, n_kv_heads=3), M.LLAMA_ERR_SHAPE),    # hd 85: odd
+    (dict(n_heads=8, n_kv_heads=3), M.LLAMA_ERR_SHAPE),              # heads % kv_heads
+    (dict(dim=640, n_heads=8, n_kv_heads=4), M.LLAMA_ERR_UNSUPPORTED),  # hd 80
+    (dict(n_heads=8, n_kv_heads=8, dim=256 * 8 * 4), M.LLAMA_ERR_UNSUPPORTED),  # hd 256
+    (dict(dtype=7), M.LLAMA_ERR_ARG),
+    (dict(dim=0), M.LLAMA_ERR_ARG),
+])
+def test_model_validation_errors(kw, code):
+    assert _call_layer(_args(**kw)) == code
+    assert M.last_error()
+
+
+def test_argument_errors_return_before_hip():
+    a = _args()
+    assert _call_layer(a, x=None) == M.LLAMA_ERR_ARG
+    assert _call_layer(a, ws=None) == M.LLAMA_ERR_ARG
+    assert _call_layer(a, start=3) == M.LLAMA_ERR_ARG  # start_pos > 0 needs a cache
+    assert _call_layer(a, batch=0) == M.LLAMA_ERR_ARG
+    kv = M.llama_kv(0x1000, 0x1000)
+    assert _call_layer(a, kv=ctypes.byref(kv), batch=5) == M.LLAMA_ERR_SHAPE  # > max_batch_size
+    assert _call_layer(a, kv=ctypes.byref(kv), start=60, seq=8) == M.LLAMA_ERR_SHAPE  # > max_seq_len
+    need = M.llama_workspace_bytes(a, 1, 8)
+    assert _call_layer(a, ws_bytes=1024) == M.LLAMA_ERR_WORKSPACE
+    assert "workspace" in M.last_error()
+    assert need > 1024
+
+
+def test_decode_and_head_argument_errors():
+    a = _args()
+    L = M.lib()
+    layers = (M.llama_layer_w * 2)(_layer_fake(), _layer_fake())
+    model = M.llama_model_w(0x1000, ctypes.cast(layers, ctypes.POINTER(M.llama_layer_w)), 0x1000, 0x1000)
+    kvs = (M.llama_kv * 2)(M.llama_kv(0x1000, 0x1000), M.llama_kv(0x1000, 0x1000))
+    rc = L.llama_decode_step(ctypes.byref(a), ctypes.byref(model), FAKE, None, 2, kvs, None, FAKE, FAKE, 1 << 40, None)
+    assert rc == M.LLAMA_ERR_ARG  # pos is NULL
+    rc = L.llama_decode_step(ctypes.byref(a), ctypes.byref(model), FAKE, FAKE, 9, kvs, None, FAKE, FAKE, 1 << 40, None)
+    assert rc == M.LLAMA_ERR_SHAPE  # batch > max_batch_size
+    rc = L.llama_decode_step(ctypes.byref(a), ctypes.byref(model), FAKE, FAKE, 2, kvs, None, FAKE, FAKE, 64, None)
+    assert rc == M.LLAMA_ERR_WORKSPACE
+    rc = L.lm_head_argmax(ctypes.byref(a), FAKE, None, FAKE, 0, None, FAKE, FAKE, 1 << 40, None)
+    assert rc == M.LLAMA_ERR_ARG  # M < 1
+    rc = L.llama_prefill(ctypes.byref(a), ctypes.byref(model), None, 1, 8, None, None, None, FAKE, FAKE, 1 << 40, None)
+    assert rc == M.LLAMA_ERR_ARG  # ids NULL
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="forces the no-device path; only meaningful without a GPU")
+def test_no_device_reports_hip_error():
+    a = _args()
+    need = M.llama_workspace_bytes(a, 1, 8)
+    rc = _call_layer(a, ws_bytes=need, ws=ctypes.c_void_p(0x10000))
+    assert rc == M.LLAMA_ERR_HIP
+    assert M.last_error()

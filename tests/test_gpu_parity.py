@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Needs an MI355X and the built library."""
+import numpy as np
+import pytest
+import torch
+
+import dense_decoder_only_rmsnorm_amd as M
+import inputs as I
+from dense_decoder_only_rmsnorm_amd import runtime as R
+from gpu_util import BF16_TOL, F32_TOL, assert_argmax, assert_close, host, say
+from oracle import llama as OL
+from oracle import runner as OR
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def small_cfg(dtype, D, H, G, S, B=1, L=1, V=1000, norm_std=0.1, seed=11, multiple_of=64):
+    return I.Config(f"small-{dtype}-{D}-{H}-{G}", dim=D, n_layers=L, n_heads=H, n_kv_heads=G, vocab_size=V,
+                    multiple_of=multiple_of, ffn_dim_multiplier=None, norm_eps=1e-5, rope_theta=500000.0,
+                    dtype=dtype, batch=B, seq_len=S, seed=seed, norm_std=norm_std, kind="layer")
+
+
+LAYER_CASES = [
+    ("bf16", 256, 4, 2, 100, 2),    # hd 64, n_rep 2, ragged tiles
+    ("bf16", 384, 4, 1, 130, 1),    # hd 96, n_rep 4
+    ("bf16", 512, 4, 4, 70, 1),     # hd 128, MHA
+    ("bf16", 1024, 8, 1, 200, 1),   # hd 128, MQA (n_rep 8)
+    ("bf16", 1024, 8, 2, 300, 2),   # hd 128, n_rep 4, several 256-row tiles
+    ("f32", 256, 4, 2, 100, 2),
+    ("f32", 384, 4, 1, 65, 1),
+    ("f32", 512, 4, 4, 70, 1),
+]
+
+
+@pytest.mark.parametrize("dtype,D,H,G,S,B", LAYER_CASES)
+def test_layer_forward_small(dtype, D, H, G, S, B):
+    cfg = small_cfg(dtype, D, H, G, S, B)
+    say(f"case layer {cfg.key} S={S} B={B}")
+    dm = R.DeviceModel(cfg, with_head=False)
+    x = I.hidden_x(cfg)
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    cap = S
+    kv = R.kv_caches(cfg, 1, B, cap)[0]
+    args = R.args_for(cfg, max_batch=B, max_seq=cap)
+    ws = R.workspace(args, B, S)
+    M.llama_layer_forward(args, dm.layers[0], xd, y, B, S, 0, kv=kv, ws=ws)
+    torch.cuda.synchronize()
+    ref = OR.layer(cfg, x, taps=True)
+    tol = BF16_TOL if cfg.bf16 else F32_TOL
+    assert_close(host(y), ref["y"], tol, "layer output")
+    for b in range(B):
+        t = ref["taps"][b]
+        assert_close(host(kv[0][b]), t["k"], tol, f"k cache (rotated) seq {b}")
+        assert_close(host(kv[1][b]), t["v"], tol, f"v cache seq {b}")
+
+
+def test_layer_forward_in_place_without_cache():
+    cfg = small_cfg("bf16", 512, 8, 2, 96, 1)
+    say(f"case layer in-place {cfg.key}")
+    dm = R.DeviceModel(cfg, with_head=False)
+    x = I.hidden_x(cfg)
+    xd = torch.from_numpy(x).cuda()
+    args = R.args_for(cfg, max_batch=1, max_seq=96)
+    ws = R.workspace(args, 1, 96)
+    M.llama_layer_forward(args, dm.layers[0], xd, xd, 1, 96, 0, kv=None, ws=ws)
+    torch.cuda.synchronize()
+    assert_close(host(xd), OR.layer(cfg, x)["y"], BF16_TOL, "layer output (y aliases x)")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunked_prefill_with_cache(dtype):
+    # two chunks: positions 0..S1-1, then S1..S1+S2-1 attending over the cache [P2 3.3]
+    S1, S2 = 77, 60
+    cfg = small_cfg(dtype, 512, 8, 2, S1 + S2, 2)
+    say(f"case chunked prefill {cfg.key}")
+    dm = R.DeviceModel(cfg, with_head=False)
+    x = I.hidden_x(cfg)
+    cap = 160
+    kv = R.kv_caches(cfg, 1, 2, cap)[0]
+    args = R.args_for(cfg, max_batch=2, max_seq=cap)
+    ws = R.workspace(args, 2, S1 + S2)
+    x1 = torch.from_numpy(np.ascontiguousarray(x[:, :S1])).cuda()
+    x2 = torch.from_numpy(np.ascontiguousarray(x[:, S1:])).cuda()
+    y1, y2 = torch.empty_like(x1), torch.empty_like(x2)
+    M.llama_layer_forward(args, dm.layers[0], x1, y1, 2, S1, 0, kv=kv, ws=ws)
+    M.llama_layer_forward(args, dm.layers[0], x2, y2, 2, S2, S1, kv=kv, ws=ws)
+    torch.cuda.synchronize()
+    ref = OR.layer(cfg, x)["y"]
+    tol = BF16_TOL if cfg.bf16 else F32_TOL
+    assert_close(np.concatenate([host(y1), host(y2)], axis=1), ref, tol, "chunked layer output")
+
+
+def _run_prefill(cfg, n_layers=None, kv_cap=None):
+    dm = R.DeviceModel(cfg, n_layers=n_layers)
+    B, S = cfg.batch, cfg.seq_len
+    ids = I.prompt_ids(cfg)
+    idd = torch.from_numpy(ids).cuda()
+    hidden = torch.empty((B, S, cfg.dim), dtype=torch.float32, device="cuda")
+    logits = torch.empty((B, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    nid = torch.empty(B, dtype=torch.int32, device="cuda")
+    args = dm.args
+    args.max_batch_size = B
+    args.max_seq_len = kv_cap or S
+    ws = R.workspace(args, B, S)
+    kvs = None
+    caches = None
+    if kv_cap:
+        caches = R.kv_caches(cfg, args.n_layers, B, kv_cap)
+        kvs = M.kv_array(caches)
+    M.llama_prefill(args, dm.struct, idd, B, S, kv=kvs, hidden=hidden, logits=logits, next_id=nid, ws=ws)
+    torch.cuda.synchronize()
+    return dm, ids, hidden, logits, nid, caches
+
+
+def test_prefill_c1_fp32():
+    cfg = I.CONFIGS["c1"]
+    say("case prefill c1 (fp32, 8 layers, S=256)")
+    _, ids, hidden, logits, nid, _ = _run_prefill(cfg)
+    ref = OR.prefill(cfg, ids, all_hidden=True)
+    assert_close(host(hidden), ref["hidden"], F32_TOL, "c1 final hidden")
+    assert_close(host(logits), ref["logits"], F32_TOL, "c1 logits")
+    assert_argmax(nid.cpu().numpy(), ref["logits"], "c1 argmax")
+
+
+def test_prefill_c2_bf16():
+    cfg = I.CONFIGS["c2"]
+    say("case prefill c2 (bf16, 4 layers, 4 x 1024)")
+    _, ids, hidden, logits, nid, _ = _run_prefill(cfg)
+    ref = OR.prefill(cfg, ids, all_hidden=True)
+    assert_close(host(hidden), ref["hidden"], BF16_TOL, "c2 final hidden")
+    assert_close(host(logits), ref["logits"], BF16_TOL, "c2 logits")
+    assert_argmax(nid.cpu().numpy(), ref["logits"], "c2 argmax")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_ragged_positions_match_oracle(dtype):
+    # prefill S tokens into the cache, then one decode step with per-sequence positions
+    cfg = small_cfg(dtype, 512, 8, 2, 40, 3, L=2, V=3000, seed=21).with_(kind="prefill")
+    say(f"case decode ragged {cfg.key}")
+    S, B = cfg.seq_len, cfg.batch
+    cap = 64
+    dm, ids, _, _, _, caches = _run_prefill(cfg, kv_cap=cap)
+    pos = np.array([S, S - 5, 17], dtype=np.int32)
+    new_ids = np.array([5, 77, 2999], dtype=np.int32)
+    logits = torch.empty((B, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    nid = torch.empty(B, dtype=torch.int32, device="cuda")
+    args = dm.args
+    ws = R.workspace(args, B, S)
+    M.llama_decode_step(args, dm.struct, torch.from_numpy(new_ids).cuda(), torch.from_numpy(pos).cuda(), B,
+                        M.kv_array(caches), logits=logits, next_id=nid, ws=ws)
+    torch.cuda.synchronize()
+    # oracle: caches from the oracle's own prefill, truncated to each sequence's position
+    ocaches = [[] for _ in range(B)]
+    OR.prefill(cfg, ids, caches=ocaches)
+    trunc = [[{"k": ocaches[b][l]["k"][:pos[b]], "v": ocaches[b][l]["v"][:pos[b]]} for l in range(cfg.n_layers)]
+             for b in range(B)]
+    m = OR.model_of(cfg)
+    new_kv = []
+    ref = OL.decode_step(new_ids, trunc, lambda r: m.rows("tok_embeddings", r), m.layer, m.get("norm"),
+                         m.get("output"), OR.args_of(cfg), new_kv=new_kv)
+    tol = BF16_TOL if cfg.bf16 else F32_TOL
+    assert_close(host(logits), ref["logits"], tol, "decode logits")
+    assert_argmax(nid.cpu().numpy(), ref["logits"], "decode argmax")
+    for (b, l, kn, vn) in new_kv:
+        assert_close(host(caches[l][0][b, pos[b]]), kn, tol, f"new k (seq {b}, layer {l})")
+        assert_close(host(caches[l][1][b, pos[b]]), vn, tol, f"new v (seq {b}, layer {l})")
+
+
+@pytest.mark.parametrize("M_rows", [1, 5, 64])
+def test_lm_head_argmax_8b_vocab(M_rows):
+    cfg = I.CONFIGS["c5"]
+    say(f"case lm_head_argmax M={M_rows} V=128256")
+    F = M.llama_ffn_hidden_dim(R.args_for(cfg))
+    syn = I.SyntheticModel(cfg, F)
+    w_out = syn.get("output")
+    h = I.normal(99, "lm_head_test_h", (M_rows, cfg.dim), 1.0, False)
+    args = R.args_for(cfg, max_batch=M_rows, max_seq=1)
+    hd_ = torch.from_numpy(h).cuda()
+    wd = R.to_device(w_out, True)
+    nw = R.to_device(np.ones(cfg.dim, np.float32), True)
+    logits = torch.empty((M_rows, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    am = torch.empty(M_rows, dtype=torch.int32, device="cuda")
+    ws = R.workspace(args, M_rows, 1)
+    M.lm_head_argmax(args, hd_, nw, wd, M_rows, logits=logits, argmax=am, ws=ws)
+    torch.cuda.synchronize()
+    hf = OL.rms_norm(h, np.ones(cfg.dim), cfg.norm_eps)
+    ref = OL.lm_head(hf, w_out)
+    assert_close(host(logits), ref, BF16_TOL, "lm head logits")
+    # hi/lo activations: the logits are accurate to ~1e-5 relative, far below the exemption gap
+    assert float(np.max(np.abs(host(logits) - ref))) < 1e-3
+    assert_argmax(am.cpu().numpy(), ref, "lm head argmax")
+
+
+def test_c3_layer_s17():
+    cfg = I.CONFIGS["c3_s17"]
+    say("case c3 one 8B layer, S=17")
+    dm = R.DeviceModel(cfg, with_head=False)
+    x = I.hidden_x(cfg)
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    args = R.args_for(cfg, max_batch=1, max_seq=17)
+    ws = R.workspace(args, 1, 17)
+    M.llama_layer_forward(args, dm.layers[0], xd, y, 1, 17, 0, kv=None, ws=ws)
+    torch.cuda.synchronize()
+    assert_close(host(y), OR.layer(cfg, x)["y"], BF16_TOL, "c3 s17 layer output")
+
+
+def test_c3_layer_s2048_sampled_rows():
+    cfg = I.CONFIGS["c3_s2048"]
+    say("case c3 one 8B layer, S=2048 (rows sampled)")
+    dm = R.DeviceModel(cfg, with_head=False)
+    x = I.hidden_x(cfg)
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    args = R.args_for(cfg, max_batch=1, max_seq=2048)
+    ws = R.workspace(args, 1, 2048)
+    M.llama_layer_forward(args, dm.layers[0], xd, y, 1, 2048, 0, kv=None, ws=ws)
+    torch.cuda.synchronize()
+    rows = [0, 1, 63, 64, 255, 1000, 1537, 2047]
+    ref = OR.layer(cfg, x, rows=rows)["y"]
+    assert_close(host(y)[:, rows], ref, BF16_TOL, "c3 s2048 sampled rows")
