@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Prefill and decode tokens/s of the Llama-3-8B-shaped decoder on one MI355X.
+
+Workloads (seeded synthetic inputs, random-init weights N(0, 0.02^2) in bf16):
+  prefill  32 layers, dim 4096, 32 heads / 8 KV heads, FFN 14336, vocab
+           128256; batch 1 x 8192 tokens; final norm, LM head and argmax of
+           the last position.  One step = one llama_prefill call.
+  decode   the same model; 64 sequences, each with a seeded KV cache of 4096
+           positions; one new token per sequence at position 4096.  One step
+           = one llama_decode_step call.
+
+Prints ONE JSON line on stdout; progress goes to stderr.  ``value`` is the
+prefill throughput (tokens/s); the decode throughput and both roofline
+fractions are in the same line.  Timing: W untimed warmup steps, then K steps
+bracketed by device synchronisation, timed with HIP events on the stream the
+library launches on.  Per-kernel durations come from a second, instrumented
+pass of K steps (llama_timing_enable), so the headline timing carries no
+instrumentation.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one workload only (profiling); the JSON line then omits the other")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def time_steps(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def kernel_times(fn, steps, M, torch):
+    torch.cuda.synchronize()
+    M.llama_timing_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    rep = M.llama_timing_report()
+    M.llama_timing_enable(False)
+    return {k: {"launches": n // steps, "ms_per_step": ms / steps, "avg_ms": ms / n} for k, (n, ms) in rep.items()}
+
+
+def cpu_threads():
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas = [i for i in info if i.get("user_api") == "blas"]
+        if blas:
+            return int(blas[0]["num_threads"])
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline_prefill(cfg, F):
+    """fp64 oracle on a bounded sample of the prefill workload."""
+    import numpy as np
+
+    import inputs as I
+    from oracle import llama as OL
+    from oracle import runner as OR
+
+    S_s, L_s = 2048, 8
+    syn = I.SyntheticModel(cfg, F)
+    ids = I.prompt_ids(cfg)[:, :S_s]
+    emb = syn.rows("tok_embeddings", ids[0])
+    layers = [syn.layer(l) for l in range(L_s)]
+    a = OR.args_of(cfg)
+    a["n_layers"] = L_s
+    h = emb
+    t0 = time.perf_counter()
+    for l in range(L_s):
+        lw = {k: OL._f64(v) for k, v in layers[l].items()}
+        h = OL.layer_forward(h, lw, a, np.arange(S_s))
+    t = time.perf_counter() - t0
+    per_layer = t / L_s
+    tok_s = S_s / (per_layer * cfg.n_layers)
+    return {"value": tok_s, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle prefill of the first {S_s} tokens through {L_s} of the {cfg.n_layers} layers "
+                      f"({t:.1f} s), scaled to all layers; weights generated beforehand, LM head excluded",
+            "seconds": t}
+
+
+def cpu_baseline_decode(cfg, F):
+    import numpy as np
+
+    import inputs as I
+    from oracle import llama as OL
+    from oracle import runner as OR
+
+    B_s, L_s = 32, 8
+    syn = I.SyntheticModel(cfg, F)
+    ids = I.prompt_ids(cfg).reshape(-1)[:B_s]
+    emb = syn.rows("tok_embeddings", ids)
+    layers = [syn.layer(l) for l in range(L_s)]
+    caches = [[{"k": I.kv_cache_block(cfg, l, "k", b, b + 1)[0], "v": I.kv_cache_block(cfg, l, "v", b, b + 1)[0]}
+               for l in range(L_s)] for b in range(B_s)]
+    a = OR.args_of(cfg)
+    t0 = time.perf_counter()
+    for l in range(L_s):
+        lw = {k: OL._f64(v) for k, v in layers[l].items()}
+        for b in range(B_s):
+            c = caches[b][l]
+            cache = {"k": c["k"], "v": c["v"]}
+            OL.layer_forward(emb[b:b + 1], lw, a, np.array([cfg.cache_len]), cache=cache)
+    t = time.perf_counter() - t0
+    tok_s = B_s / (t / L_s * cfg.n_layers)
+    return {"value": tok_s, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle decode of {B_s} sequences (cache 4096) through {L_s} of the {cfg.n_layers} "
+                      f"layers ({t:.1f} s), scaled to all layers; LM head excluded",
+            "seconds": t}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("bench.py measures one GPU only: this build runs the whole forward pass on a single MI355X "
+               "(multi-GPU sharding is described in DESIGN.md, not implemented); rerun with --gpus 1")
+        log(msg)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dense_decoder_only_rmsnorm_amd as M
+    import inputs as I
+    from dense_decoder_only_rmsnorm_amd import runtime as R
+
+    torch.cuda.set_device(0)
+    c4, c5 = I.CONFIGS["c4"], I.CONFIGS["c5"]
+    t0 = time.time()
+    log("generating and uploading the 8B-shaped weights (seed of the prefill configuration) ...")
+    dm = R.DeviceModel(c4)
+    F = dm.F
+    log(f"  weights ready in {time.time() - t0:.1f} s (F={F})")
+    out = {}
+    kern = {}
+
+    def summarize(ktimes):
+        return {k: round(v["avg_ms"], 5) for k, v in sorted(ktimes.items(), key=lambda kv: -kv[1]["ms_per_step"])}
+
+    if args.only in (None, "prefill"):
+        B, S = c4.batch, c4.seq_len
+        pa = R.args_for(c4, max_batch=B, max_seq=S)
+        ids = torch.from_numpy(I.prompt_ids(c4)).cuda()
+        logits = torch.empty((B, c4.vocab_size), dtype=torch.float32, device="cuda")
+        nid = torch.empty(B, dtype=torch.int32, device="cuda")
+        ws = R.workspace(pa, B, S)
+
+        def prefill():
+            M.llama_prefill(pa, dm.struct, ids, B, S, kv=None, logits=logits, next_id=nid, ws=ws)
+
+        ms = time_steps(prefill, args.steps, args.warmup, torch)
+        kt = kernel_times(prefill, args.steps, M, torch)
+        kern["prefill"] = kt
+        log(f"prefill: {ms:.3f} ms/step, {B * S / (ms / 1e3):.0f} tokens/s")
+        for k, v in sorted(kt.items(), key=lambda kv: -kv[1]["ms_per_step"]):
+            log(f"  {k:22s} {v['launches']:5d} launches  {v['ms_per_step']:9.3f} ms/step  avg {v['avg_ms']:.4f} ms")
+        # dominant kernel: the fused w1/w3 SwiGLU GEMM (47% of the layer FLOPs)
+        dk = kt["gemm_w1w3_swiglu"]
+        flop = 2.0 * B * S * c4.dim * (2 * F)
+        ach = flop / (dk["avg_ms"] / 1e3) / 1e12
+        total_flop = 0.0
+        D, Hq, Hk = c4.dim, c4.n_heads * c4.head_dim, c4.n_kv_heads * c4.head_dim
+        T = B * S
+        per_layer = 2.0 * T * D * (Hq + 2 * Hk) + 2.0 * T * Hq * D + 2.0 * T * D * 2 * F + 2.0 * T * F * D
+        attn = 4.0 * c4.head_dim * c4.n_heads * B * (S * (S + 1) / 2)
+        total_flop = c4.n_layers * (per_layer + attn) + 2.0 * B * D * c4.vocab_size
+        out["prefill"] = dict(ms=ms, tok_s=B * S / (ms / 1e3), step_tflops=total_flop / (ms / 1e3) / 1e12,
+                              roofline={"kernel": "gemm_w1w3_swiglu", "bound": "mfma", "achieved": round(ach, 2),
+                                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                        "flop_per_launch": flop, "avg_launch_ms": dk["avg_ms"]})
+        del ws, logits, ids
+        torch.cuda.empty_cache()
+
+    if args.only in (None, "decode"):
+        B, P, cap = c5.batch, c5.cache_len, c5.cache_cap
+        t1 = time.time()
+        log("generating and uploading the seeded KV caches (32 layers x 64 x 4096 x 8 x 128, K and V) ...")
+        caches = []
+        for l in range(c5.n_layers):
+            pair = []
+            for which in ("k", "v"):
+                t = torch.zeros((B, cap, c5.n_kv_heads, c5.head_dim), dtype=torch.bfloat16, device="cuda")
+                t[:, :P] = R.bits_to_device(I.kv_cache_bits(c5, l, which))
+                pair.append(t)
+            caches.append(tuple(pair))
+        log(f"  caches ready in {time.time() - t1:.1f} s")
+        kvs = M.kv_array(caches)
+        da = R.args_for(c5, max_batch=B, max_seq=cap)
+        ids = torch.from_numpy(I.prompt_ids(c5).reshape(-1).astype(np.int32)).cuda()
+        pos = torch.full((B,), P, dtype=torch.int32, device="cuda")
+        logits = torch.empty((B, c5.vocab_size), dtype=torch.float32, device="cuda")
+        nid = torch.empty(B, dtype=torch.int32, device="cuda")
+        ws = R.workspace(da, B, 1)
+
+        def decode():
+            M.llama_decode_step(da, dm.struct, ids, pos, B, kvs, logits=logits, next_id=nid, ws=ws)
+
+        dsteps = max(args.steps, 10)
+        ms = time_steps(decode, dsteps, args.warmup, torch)
+        kt = kernel_times(decode, dsteps, M, torch)
+        kern["decode"] = kt
+        log(f"decode: {ms:.3f} ms/step, {B / (ms / 1e3):.0f} tokens/s")
+        for k, v in sorted(kt.items(), key=lambda kv: -kv[1]["ms_per_step"]):
+            log(f"  {k:22s} {v['launches']:5d} launches  {v['ms_per_step']:9.3f} ms/step  avg {v['avg_ms']:.4f} ms")
+        dk = kt["attn_decode"]
+        kv_bytes = 2.0 * B * (P + 1) * c5.n_kv_heads * c5.head_dim * 2
+        ach = kv_bytes / (dk["avg_ms"] / 1e3) / 1e9
+        D, Hq, Hk = c5.dim, c5.n_heads * c5.head_dim, c5.n_kv_heads * c5.head_dim
+        w_layer = 2.0 * (D * (Hq + 2 * Hk) + Hq * D + 3 * D * F + 2 * D)
+        step_bytes = c5.n_layers * (w_layer + kv_bytes) + 2.0 * c5.vocab_size * D + 2.0 * D
+        out["decode"] = dict(ms=ms, tok_s=B / (ms / 1e3), step_gbs=step_bytes / (ms / 1e3) / 1e9,
+                             step_frac=step_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                             roofline={"kernel": "attn_decode", "bound": "hbm", "achieved": round(ach, 1),
+                                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                                       "traffic": None, "bytes_per_launch": kv_bytes, "avg_launch_ms": dk["avg_ms"]})
+        del caches, kvs, ws
+        torch.cuda.empty_cache()
+
+    cpu = {}
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on bounded samples (cpu_baseline) ...")
+        if "prefill" in out:
+            cpu["prefill"] = cpu_baseline_prefill(c4, F)
+            log(f"  prefill oracle: {cpu['prefill']['value']:.2f} tokens/s ({cpu['prefill']['seconds']:.1f} s)")
+        if "decode" in out:
+            cpu["decode"] = cpu_baseline_decode(c5, F)
+            log(f"  decode oracle: {cpu['decode']['value']:.3f} tokens/s ({cpu['decode']['seconds']:.1f} s)")
+
+    head = "prefill" if "prefill" in out else "decode"
+    res = {
+        "metric": "prefill & decode tokens/s, Llama-3-8B-shaped layers, 1 MI355X; % of roofline",
+        "value": round(out[head]["tok_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(out[head]["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02^2) bf16 weights, uniform token ids, N(0,1) KV cache)",
+        "config": {"workload": ("llama3-8b-shape prefill B1xS8192 (value) + decode B64 over KV 4096"
+                                if len(out) == 2 else f"llama3-8b-shape {head}"),
+                   "prefill": {"batch": 1, "seq_len": 8192, "layers": 32, "vocab": 128256},
+                   "decode": {"batch": 64, "cache_len": 4096, "layers": 32, "vocab": 128256}},
+        "roofline": {k: v for k, v in out[head]["roofline"].items()},
+    }
+    if head == "prefill" and "decode" in out:
+        d = out["decode"]
+        res["decode"] = {"value": round(d["tok_s"], 1), "unit": "tokens/s", "ms_per_step": round(d["ms"], 4),
+                         "step_hbm_frac": round(d["step_frac"], 4), "roofline": d["roofline"]}
+    if head == "prefill":
+        res["prefill_step_tflops"] = round(out["prefill"]["step_tflops"], 1)
+        res["prefill_step_mfma_frac"] = round(out["prefill"]["step_tflops"] / PEAK_BF16_TFLOPS, 4)
+    if cpu:
+        c = cpu.get(head)
+        res["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items() if k != "seconds"}
+        res["cpu_baseline"]["cpu"] = platform.processor() or platform.machine()
+        if head == "prefill" and "decode" in cpu:
+            res["decode"]["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                             for k, v in cpu["decode"].items() if k != "seconds"}
+    res["kernels_avg_ms"] = {w: summarize(k) for w, k in kern.items()}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

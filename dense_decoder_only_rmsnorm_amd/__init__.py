@@ -25,7 +25,7 @@ LLAMA_F32, LLAMA_BF16 = 0, 1
 ERROR_NAMES = {-1: "LLAMA_ERR_ARG", -2: "LLAMA_ERR_SHAPE", -3: "LLAMA_ERR_UNSUPPORTED", -4: "LLAMA_ERR_WORKSPACE",
                -5: "LLAMA_ERR_HIP"}
 EXPORTED = ("llama_ffn_hidden_dim", "llama_workspace_bytes", "llama_layer_forward", "llama_prefill",
-            "llama_decode_step", "lm_head_argmax", "llama_last_error")
+            "llama_decode_step", "lm_head_argmax", "llama_last_error", "llama_timing_enable", "llama_timing_report")
 
 
 class LlamaError(RuntimeError):
@@ -84,6 +84,10 @@ def lib() -> ctypes.CDLL:
         L.llama_decode_step.restype = ctypes.c_int
         L.lm_head_argmax.argtypes = [A, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         L.lm_head_argmax.restype = ctypes.c_int
+        L.llama_timing_enable.argtypes = [ctypes.c_int]
+        L.llama_timing_enable.restype = ctypes.c_int
+        L.llama_timing_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+        L.llama_timing_report.restype = ctypes.c_int64
         L.llama_last_error.argtypes = []
         L.llama_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -187,7 +191,23 @@ def lm_head_argmax(args: llama_args, h, final_norm_w, w_out, M: int, logits=None
     _check(rc)
 
 
-__all__ = ["lib", "last_error", "LlamaError", "llama_args", "llama_layer_w", "llama_model_w", "llama_kv",
+def llama_timing_enable(on: bool = True):
+    _check(lib().llama_timing_enable(1 if on else 0))
+
+
+def llama_timing_report() -> dict:
+    """{kernel_name: (launches, total_ms)} since the last enable/report."""
+    buf = ctypes.create_string_buffer(1 << 20)
+    n = lib().llama_timing_report(buf, len(buf))
+    _check(min(int(n), 0))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out
+
+
+__all__ = ["llama_timing_enable", "llama_timing_report", "lib", "last_error", "LlamaError", "llama_args", "llama_layer_w", "llama_model_w", "llama_kv",
            "make_args", "layer_struct", "model_struct", "kv_array", "llama_ffn_hidden_dim",
            "llama_workspace_bytes", "llama_layer_forward", "llama_prefill", "llama_decode_step", "lm_head_argmax",
            "LLAMA_F32", "LLAMA_BF16", "EXPORTED"]

@@ -5,9 +5,13 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "kernels.h"
 #include "llama_mi355x.h"
@@ -33,6 +37,58 @@ int fail(int code, const char *fmt, ...) {
   do {                                                                                      \
     hipError_t e_ = (expr);                                                                 \
     if (e_ != hipSuccess) return fail(LLAMA_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// Optional per-kernel timing (llama_timing_enable / llama_timing_report): when
+// on, every launch is bracketed by two hipEvents recorded on its stream.
+// ---------------------------------------------------------------------------
+struct TimingRec {
+  const char *name;
+  hipEvent_t start, stop;
+};
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TimingRec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  hipEvent_t get() {
+    if (used == pool.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+Timing g_timing;
+
+struct TimingScope {
+  const char *name;
+  hipStream_t s;
+  hipEvent_t start = nullptr;
+  TimingScope(const char *n, hipStream_t st) : name(n), s(st) {
+    if (!g_timing.on) return;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    start = g_timing.get();
+    if (start) hipEventRecord(start, s);
+  }
+  ~TimingScope() {
+    if (!start) return;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    hipEvent_t stop = g_timing.get();
+    if (!stop) return;
+    hipEventRecord(stop, s);
+    g_timing.recs.push_back({name, start, stop});
+  }
+};
+
+// launch with a timing tag; returns LLAMA_ERR_HIP from the enclosing function on failure
+#define LAUNCH(tag, expr)         \
+  do {                            \
+    TimingScope ts_((tag), s);    \
+    HIPCHK(expr);                 \
   } while (0)
 
 constexpr int kDecodeChunk = 256;  // keys per decode-attention chunk
@@ -255,7 +311,7 @@ int rmsnorm(const Dims &d, int mode, float *h, int64_t in_off, int64_t in_stride
   na.D = d.D;
   na.out = out;
   na.out_plane = out_plane;
-  HIPCHK(launch_rmsnorm(d.dt, mode, na, rows, s));
+  LAUNCH("rmsnorm", launch_rmsnorm(d.dt, mode, na, rows, s));
   return LLAMA_OK;
 }
 
@@ -278,15 +334,15 @@ int run_head(const Dims &d, const HeadWs &hw, const void *w_out, int M, float *l
       sa.pval = hw.pval + (int64_t)r0 * hw.nblk;
       sa.pidx = hw.pidx + (int64_t)r0 * hw.nblk;
       sa.nblk = hw.nblk;
-      HIPCHK(launch_skinny(SK_LOGITS, sa, s));
+      LAUNCH("lm_head", launch_skinny(SK_LOGITS, sa, s));
     }
   } else {
     float *lg = logits ? logits : hw.logits;
-    HIPCHK(launch_gemm_f32(EPI_STORE_F32, hw.hf32, static_cast<const float *>(w_out), lg, d.V, nullptr, 0, M, d.V, d.D,
+    LAUNCH("lm_head", launch_gemm_f32(EPI_STORE_F32, hw.hf32, static_cast<const float *>(w_out), lg, d.V, nullptr, 0, M, d.V, d.D,
                            s));
-    HIPCHK(launch_argmax_partial(lg, M, d.V, 4096, hw.pval, hw.pidx, hw.nblk, s));
+    LAUNCH("argmax_partial", launch_argmax_partial(lg, M, d.V, 4096, hw.pval, hw.pidx, hw.nblk, s));
   }
-  HIPCHK(launch_argmax_reduce(hw.pval, hw.pidx, M, hw.nblk, ids, s));
+  LAUNCH("argmax_reduce", launch_argmax_reduce(hw.pval, hw.pidx, M, hw.nblk, ids, s));
   return LLAMA_OK;
 }
 
@@ -299,7 +355,7 @@ int run_layer_prefill(const llama_args *a, const Dims &d, const llama_layer_w *l
   const int cap = kv ? a->max_seq_len : S;
   void *kc = kv ? kv->k : w.k;
   void *vc = kv ? kv->v : w.v;
-  if (!table_ready) HIPCHK(launch_rope_table(w.tab, nullptr, start_pos, INT32_MAX, S, d.hd, a->rope_theta, s));
+  if (!table_ready) LAUNCH("rope_table", launch_rope_table(w.tab, nullptr, start_pos, INT32_MAX, S, d.hd, a->rope_theta, s));
 
   if (d.dt == LLAMA_BF16) {
     // a2: attention_norm -> bf16
@@ -329,17 +385,17 @@ int run_layer_prefill(const llama_args *a, const Dims &d, const llama_layer_w *l
     g.q = static_cast<u16 *>(w.q);
     g.kc = kc;
     g.vc = vc;
-    HIPCHK(launch_gemm_bf16(EPI_QKV_ROPE, g, s));
+    LAUNCH("gemm_qkv_rope", launch_gemm_bf16(EPI_QKV_ROPE, g, s));
   } else {
     if (int e = rmsnorm(d, 0, const_cast<float *>(x_in), 0, d.D, nullptr, 0, 0, lw->attention_norm, a->norm_eps,
                         w.xn, 0, T, s))
       return e;
     const float *xn = static_cast<const float *>(w.xn);
-    HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wq), w.qkv, d.Nqkv(), nullptr, 0, T,
+    LAUNCH("gemm_qkv", launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wq), w.qkv, d.Nqkv(), nullptr, 0, T,
                            d.Hq(), d.D, s));
-    HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wk), w.qkv + d.Hq(), d.Nqkv(), nullptr,
+    LAUNCH("gemm_qkv", launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wk), w.qkv + d.Hq(), d.Nqkv(), nullptr,
                            0, T, d.Hk(), d.D, s));
-    HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wv), w.qkv + d.Hq() + d.Hk(), d.Nqkv(),
+    LAUNCH("gemm_qkv", launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wv), w.qkv + d.Hq() + d.Hk(), d.Nqkv(),
                            nullptr, 0, T, d.Hk(), d.D, s));
     RopeQkvArgs ra{};
     ra.part = w.qkv;
@@ -358,7 +414,7 @@ int run_layer_prefill(const llama_args *a, const Dims &d, const llama_layer_w *l
     ra.qout = static_cast<float *>(w.q);
     ra.kc = kc;
     ra.vc = vc;
-    HIPCHK(launch_rope_qkv(d.dt, ra, s));
+    LAUNCH("rope_qkv", launch_rope_qkv(d.dt, ra, s));
   }
   // a6: causal GQA attention
   AttnArgs at{};
@@ -375,7 +431,7 @@ int run_layer_prefill(const llama_args *a, const Dims &d, const llama_layer_w *l
   at.hd = d.hd;
   at.start_pos = start_pos;
   at.scale = (float)(1.0 / sqrt((double)d.hd));
-  HIPCHK(launch_attn_prefill(d.dt, at, s));
+  LAUNCH("attn_prefill", launch_attn_prefill(d.dt, at, s));
 
   if (d.dt == LLAMA_BF16) {
     // a8: h = x + o wo^T
@@ -391,7 +447,7 @@ int run_layer_prefill(const llama_args *a, const Dims &d, const llama_layer_w *l
     g.ldc = d.D;
     g.R = x_in;
     g.ldr = d.D;
-    HIPCHK(launch_gemm_bf16(EPI_RESID, g, s));
+    LAUNCH("gemm_wo_resid", launch_gemm_bf16(EPI_RESID, g, s));
     // a2: ffn_norm
     if (int e = rmsnorm(d, 1, h, 0, d.D, nullptr, 0, 0, lw->ffn_norm, a->norm_eps, w.xn, 0, T, s)) return e;
     // a9: u = silu(xn2 w1^T) * (xn2 w3^T)
@@ -406,7 +462,7 @@ int run_layer_prefill(const llama_args *a, const Dims &d, const llama_layer_w *l
     f.K = d.D;
     f.C = w.u;
     f.ldc = d.F;
-    HIPCHK(launch_gemm_bf16(EPI_SWIGLU, f, s));
+    LAUNCH("gemm_w1w3_swiglu", launch_gemm_bf16(EPI_SWIGLU, f, s));
     // a10: h += u w2^T
     GemmArgs g2{};
     g2.A = static_cast<const u16 *>(w.u);
@@ -420,18 +476,18 @@ int run_layer_prefill(const llama_args *a, const Dims &d, const llama_layer_w *l
     g2.ldc = d.D;
     g2.R = h;
     g2.ldr = d.D;
-    HIPCHK(launch_gemm_bf16(EPI_RESID, g2, s));
+    LAUNCH("gemm_w2_resid", launch_gemm_bf16(EPI_RESID, g2, s));
   } else {
-    HIPCHK(launch_gemm_f32(EPI_RESID, static_cast<const float *>(w.o), static_cast<const float *>(lw->wo), h, d.D,
+    LAUNCH("gemm_wo_resid", launch_gemm_f32(EPI_RESID, static_cast<const float *>(w.o), static_cast<const float *>(lw->wo), h, d.D,
                            x_in, d.D, T, d.D, d.Hq(), s));
     if (int e = rmsnorm(d, 0, h, 0, d.D, nullptr, 0, 0, lw->ffn_norm, a->norm_eps, w.xn, 0, T, s)) return e;
     const float *xn = static_cast<const float *>(w.xn);
-    HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->w1), w.gate, d.F, nullptr, 0, T, d.F, d.D,
+    LAUNCH("gemm_w1w3", launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->w1), w.gate, d.F, nullptr, 0, T, d.F, d.D,
                            s));
-    HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->w3), w.up, d.F, nullptr, 0, T, d.F, d.D,
+    LAUNCH("gemm_w1w3", launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->w3), w.up, d.F, nullptr, 0, T, d.F, d.D,
                            s));
-    HIPCHK(launch_swiglu(w.gate, w.up, static_cast<float *>(w.u), (int64_t)T * d.F, s));
-    HIPCHK(launch_gemm_f32(EPI_RESID, static_cast<const float *>(w.u), static_cast<const float *>(lw->w2), h, d.D, h,
+    LAUNCH("swiglu", launch_swiglu(w.gate, w.up, static_cast<float *>(w.u), (int64_t)T * d.F, s));
+    LAUNCH("gemm_w2_resid", launch_gemm_f32(EPI_RESID, static_cast<const float *>(w.u), static_cast<const float *>(lw->w2), h, d.D, h,
                            d.D, T, d.D, d.F, s));
   }
   return LLAMA_OK;
@@ -515,8 +571,8 @@ int llama_prefill(const llama_args *a, const llama_model_w *w, const int32_t *id
   float *h = hidden ? hidden : pw.h;
   const int T = batch * seq_len;
   // a1: embedding rows
-  HIPCHK(launch_embed(d.dt, ids, w->tok_embeddings, h, T, d.D, d.V, s));
-  HIPCHK(launch_rope_table(pw.tab, nullptr, 0, INT32_MAX, seq_len, d.hd, a->rope_theta, s));
+  LAUNCH("embed", launch_embed(d.dt, ids, w->tok_embeddings, h, T, d.D, d.V, s));
+  LAUNCH("rope_table", launch_rope_table(pw.tab, nullptr, 0, INT32_MAX, seq_len, d.hd, a->rope_theta, s));
   // a2-a11: layers
   for (int l = 0; l < d.L; ++l) {
     if (int e = run_layer_prefill(a, d, &w->layers[l], h, h, batch, seq_len, 0, kv ? &kv[l] : nullptr, pw, true, s))
@@ -564,8 +620,8 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
   const int B = batch;
   const bool bf = d.dt == LLAMA_BF16;
 
-  HIPCHK(launch_embed(d.dt, ids, w->tok_embeddings, dw.h, B, d.D, d.V, s));
-  HIPCHK(launch_rope_table(dw.tab, pos, 0, cap - 1, B, d.hd, a->rope_theta, s));
+  LAUNCH("embed", launch_embed(d.dt, ids, w->tok_embeddings, dw.h, B, d.D, d.V, s));
+  LAUNCH("rope_table", launch_rope_table(dw.tab, pos, 0, cap - 1, B, d.hd, a->rope_theta, s));
   const float *pend = nullptr;  // w2 partials of the previous layer still to fold into h
   int pend_n = 0;
   for (int l = 0; l < d.L; ++l) {
@@ -592,14 +648,14 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
       sa.ksplit = dw.ks1;
       sa.C = dw.qkv_part;
       sa.c_plane = (int64_t)B * d.Nqkv();
-      HIPCHK(launch_skinny(SK_PARTIAL, sa, s));
+      LAUNCH("skinny_qkv", launch_skinny(SK_PARTIAL, sa, s));
     } else {
       const float *xn = static_cast<const float *>(dw.xn);
-      HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wq), dw.qkv_part, d.Nqkv(), nullptr, 0,
+      LAUNCH("gemm_qkv", launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wq), dw.qkv_part, d.Nqkv(), nullptr, 0,
                              B, d.Hq(), d.D, s));
-      HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wk), dw.qkv_part + d.Hq(), d.Nqkv(),
+      LAUNCH("gemm_qkv", launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wk), dw.qkv_part + d.Hq(), d.Nqkv(),
                              nullptr, 0, B, d.Hk(), d.D, s));
-      HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wv), dw.qkv_part + d.Hq() + d.Hk(),
+      LAUNCH("gemm_qkv", launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->wv), dw.qkv_part + d.Hq() + d.Hk(),
                              d.Nqkv(), nullptr, 0, B, d.Hk(), d.D, s));
     }
     // a4-a5: RoPE + cache write at pos[b]
@@ -620,7 +676,7 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
     ra.qout = dw.q;
     ra.kc = kv[l].k;
     ra.vc = kv[l].v;
-    HIPCHK(launch_rope_qkv(d.dt, ra, s));
+    LAUNCH("rope_qkv", launch_rope_qkv(d.dt, ra, s));
     // a7: attention over the cache
     DecodeAttnArgs da{};
     da.q = dw.q;
@@ -641,7 +697,8 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
     da.out = dw.o;
     da.out_mode = bf ? 2 : 0;
     da.out_plane = (int64_t)B * d.Hq();
-    HIPCHK(launch_attn_decode(d.dt, da, s));
+    LAUNCH("attn_decode", launch_attn_decode(d.dt, da, s));
+    LAUNCH("attn_combine", launch_attn_combine(da, s));
     if (bf) {
       // a8: wo partials, folded into h by the ffn_norm kernel
       SkinnyArgs sa{};
@@ -656,7 +713,7 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
       sa.ksplit = dw.ks2;
       sa.C = dw.wo_part;
       sa.c_plane = (int64_t)B * d.D;
-      HIPCHK(launch_skinny(SK_PARTIAL, sa, s));
+      LAUNCH("skinny_wo", launch_skinny(SK_PARTIAL, sa, s));
       if (int e = rmsnorm(d, 2, dw.h, 0, d.D, dw.wo_part, dw.ks2, (int64_t)B * d.D, lw->ffn_norm, a->norm_eps, dw.xn,
                           (int64_t)B * d.D, B, s))
         return e;
@@ -674,7 +731,7 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
       fa.ksplit = 1;
       fa.C = dw.u;
       fa.c_plane = (int64_t)B * d.F;
-      HIPCHK(launch_skinny(SK_SWIGLU_HILO, fa, s));
+      LAUNCH("skinny_w1w3_swiglu", launch_skinny(SK_SWIGLU_HILO, fa, s));
       // a10: w2 partials (folded by the next norm)
       SkinnyArgs sb{};
       sb.A = static_cast<const u16 *>(dw.u);
@@ -688,20 +745,20 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
       sb.ksplit = dw.ks3;
       sb.C = dw.w2_part;
       sb.c_plane = (int64_t)B * d.D;
-      HIPCHK(launch_skinny(SK_PARTIAL, sb, s));
+      LAUNCH("skinny_w2", launch_skinny(SK_PARTIAL, sb, s));
       pend = dw.w2_part;
       pend_n = dw.ks3;
     } else {
-      HIPCHK(launch_gemm_f32(EPI_RESID, static_cast<const float *>(dw.o), static_cast<const float *>(lw->wo), dw.h,
+      LAUNCH("gemm_wo_resid", launch_gemm_f32(EPI_RESID, static_cast<const float *>(dw.o), static_cast<const float *>(lw->wo), dw.h,
                              d.D, dw.h, d.D, B, d.D, d.Hq(), s));
       if (int e = rmsnorm(d, 0, dw.h, 0, d.D, nullptr, 0, 0, lw->ffn_norm, a->norm_eps, dw.xn, 0, B, s)) return e;
       const float *xn = static_cast<const float *>(dw.xn);
-      HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->w1), dw.gate, d.F, nullptr, 0, B, d.F,
+      LAUNCH("gemm_w1w3", launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->w1), dw.gate, d.F, nullptr, 0, B, d.F,
                              d.D, s));
-      HIPCHK(launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->w3), dw.up, d.F, nullptr, 0, B, d.F,
+      LAUNCH("gemm_w1w3", launch_gemm_f32(EPI_STORE_F32, xn, static_cast<const float *>(lw->w3), dw.up, d.F, nullptr, 0, B, d.F,
                              d.D, s));
-      HIPCHK(launch_swiglu(dw.gate, dw.up, static_cast<float *>(dw.u), (int64_t)B * d.F, s));
-      HIPCHK(launch_gemm_f32(EPI_RESID, static_cast<const float *>(dw.u), static_cast<const float *>(lw->w2), dw.h,
+      LAUNCH("swiglu", launch_swiglu(dw.gate, dw.up, static_cast<float *>(dw.u), (int64_t)B * d.F, s));
+      LAUNCH("gemm_w2_resid", launch_gemm_f32(EPI_RESID, static_cast<const float *>(dw.u), static_cast<const float *>(lw->w2), dw.h,
                              d.D, dw.h, d.D, B, d.D, d.F, s));
     }
   }
@@ -742,5 +799,44 @@ int lm_head_argmax(const llama_args *a, const float *h, const void *final_norm_w
 }
 
 const char *llama_last_error(void) { return g_err.c_str(); }
+
+int llama_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.on = on != 0;
+  g_timing.recs.clear();
+  g_timing.used = 0;
+  return LLAMA_OK;
+}
+
+int64_t llama_timing_report(char *buf, size_t len) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  struct Agg {
+    int64_t n = 0;
+    double ms = 0.0;
+  };
+  std::map<std::string, Agg> agg;
+  for (const TimingRec &r : g_timing.recs) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) return fail(LLAMA_ERR_HIP, "hipEventSynchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return fail(LLAMA_ERR_HIP, "hipEventElapsedTime failed");
+    Agg &a = agg[r.name];
+    a.n += 1;
+    a.ms += ms;
+  }
+  std::string out;
+  char line[256];
+  for (const auto &kv : agg) {
+    snprintf(line, sizeof line, "%s %lld %.6f\n", kv.first.c_str(), (long long)kv.second.n, kv.second.ms);
+    out += line;
+  }
+  if (buf && len) {
+    const size_t n = std::min(len - 1, out.size());
+    memcpy(buf, out.data(), n);
+    buf[n] = 0;
+  }
+  g_timing.recs.clear();
+  g_timing.used = 0;
+  return (int64_t)out.size() + 1;
+}
 
 }  // extern "C"

@@ -359,9 +359,6 @@ hipError_t decode_hd(int dtype, const DecodeAttnArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((attn_decode_kernel<u16, HD>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((attn_decode_kernel<float, HD>), grid, dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<HD>, dim3(a.H, a.B), dim3(HD), 0, s, a);
   return hipGetLastError();
 }
 }  // namespace
@@ -373,6 +370,16 @@ hipError_t launch_attn_prefill(int dtype, const AttnArgs &a, hipStream_t s) {
     case 128: return prefill_hd<128>(dtype, a, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_combine(const DecodeAttnArgs &a, hipStream_t s) {
+  switch (a.hd) {
+    case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(a.H, a.B), dim3(64), 0, s, a); break;
+    case 96: hipLaunchKernelGGL(attn_combine_kernel<96>, dim3(a.H, a.B), dim3(96), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(a.H, a.B), dim3(128), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_decode(int dtype, const DecodeAttnArgs &a, hipStream_t s) {

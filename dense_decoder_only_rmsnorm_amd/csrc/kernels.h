@@ -111,5 +111,6 @@ hipError_t launch_skinny(int epi, const SkinnyArgs &a, hipStream_t s);
 
 hipError_t launch_attn_prefill(int dtype, const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_decode(int dtype, const DecodeAttnArgs &a, hipStream_t s);
+hipError_t launch_attn_combine(const DecodeAttnArgs &a, hipStream_t s);
 
 }  // namespace llk

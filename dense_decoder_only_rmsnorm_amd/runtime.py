@@ -19,6 +19,11 @@ from . import (LLAMA_BF16, LLAMA_F32, kv_array, llama_decode_step, llama_ffn_hid
 DEV = "cuda"
 
 
+def bits_to_device(bits: np.ndarray, device: str = DEV) -> torch.Tensor:
+    """Upload bf16 bit patterns (uint16) as a bfloat16 tensor."""
+    return torch.from_numpy(bits.view(np.int16)).to(device).view(torch.bfloat16)
+
+
 def to_device(a: np.ndarray, bf16: bool, device: str = DEV) -> torch.Tensor:
     """Upload float32 values; bf16 tensors get the exact bf16 bit patterns."""
     if bf16:
@@ -46,13 +51,18 @@ class DeviceModel:
         self.args.n_layers = L
         self.layers: List[dict] = []
         for l in range(L):
-            self.layers.append({k: to_device(self.syn.get(k, l), cfg.bf16, device) for k in I.LAYER_TENSORS})
+            self.layers.append({k: self._up(k, l, device) for k in I.LAYER_TENSORS})
         self.tok = self.norm = self.output = None
         if with_head:
-            self.tok = to_device(self.syn.get("tok_embeddings"), cfg.bf16, device)
-            self.norm = to_device(self.syn.get("norm"), cfg.bf16, device)
-            self.output = to_device(self.syn.get("output"), cfg.bf16, device)
+            self.tok = self._up("tok_embeddings", None, device)
+            self.norm = self._up("norm", None, device)
+            self.output = self._up("output", None, device)
         self._model = None
+
+    def _up(self, kind, layer, device):
+        if self.cfg.bf16:
+            return bits_to_device(self.syn.bits(kind, layer), device)
+        return to_device(self.syn.get(kind, layer), False, device)
 
     @property
     def struct(self):

@@ -167,6 +167,18 @@ int lm_head_argmax(const llama_args *a, const float *h, const void *final_norm_w
 /* Message describing the last non-OK return on the calling thread. */
 const char *llama_last_error(void);
 
+/* Per-kernel timing for measurement.  llama_timing_enable(1) clears the
+ * record and makes every later launch (from any entry point) record a HIP
+ * event before and after it on its stream; llama_timing_enable(0) stops
+ * recording.  llama_timing_report() waits for the recorded events, writes
+ * one line "kernel_name launches total_ms" per kernel into buf (up to len
+ * bytes, NUL-terminated, may be NULL), clears the record and returns the
+ * bytes the full report needs (or a negative llama_status).  The events are
+ * created on first use and reused; timing adds host work per launch, so
+ * time whole steps with it off. */
+int llama_timing_enable(int on);
+int64_t llama_timing_report(char *buf, size_t len);
+
 #ifdef __cplusplus
 }
 #endif

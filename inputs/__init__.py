@@ -73,8 +73,13 @@ def _draw_chunk(kind: str, seed: int, name: str, chunk: int, n: int, param):
     raise ValueError(kind)
 
 
-def _draw(kind: str, seed: int, name: str, start: int, stop: int, param=None, dtype=np.float32) -> np.ndarray:
-    """Elements [start, stop) of the flat stream for ``name``."""
+def _draw(kind: str, seed: int, name: str, start: int, stop: int, param=None, dtype=np.float32,
+          post=None) -> np.ndarray:
+    """Elements [start, stop) of the flat stream for ``name``.
+
+    ``post`` (optional) maps a chunk's raw draws to the stored values inside
+    the worker thread (scaling, rounding); the result dtype is ``dtype``.
+    """
     out = np.empty(stop - start, dtype=dtype)
     if stop <= start:
         return out
@@ -84,8 +89,8 @@ def _draw(kind: str, seed: int, name: str, start: int, stop: int, param=None, dt
         lo, hi = c * CHUNK, (c + 1) * CHUNK
         a, b = max(lo, start), min(hi, stop)
         # a stream's first n draws do not depend on how many follow
-        vals = _draw_chunk(kind, seed, name, c, b - lo, param)
-        out[a - start:b - start] = vals[a - lo:b - lo]
+        vals = _draw_chunk(kind, seed, name, c, b - lo, param)[a - lo:b - lo]
+        out[a - start:b - start] = post(vals) if post is not None else vals
 
     chunks = range(first, last + 1)
     if len(chunks) == 1:
@@ -106,9 +111,22 @@ def normal(seed: int, name: str, shape, std: float, bf16: bool, start: int = 0, 
     n = int(np.prod(shape))
     sub = stop is not None or start != 0
     stop = n if stop is None else stop
-    v = _draw("normal", seed, name, start, stop) * np.float32(std)
+    sd = np.float32(std)
     if bf16:
-        v = bf16_bits_to_f32(f32_to_bf16_bits(v))
+        post = lambda v: bf16_bits_to_f32(f32_to_bf16_bits(v * sd))  # noqa: E731
+    else:
+        post = lambda v: v * sd  # noqa: E731
+    v = _draw("normal", seed, name, start, stop, post=post)
+    return v if sub else v.reshape(shape)
+
+
+def normal_bits(seed: int, name: str, shape, std: float, start: int = 0, stop: Optional[int] = None) -> np.ndarray:
+    """The bfloat16 bit patterns (uint16) of ``normal(seed, name, shape, std, bf16=True)``."""
+    n = int(np.prod(shape))
+    sub = stop is not None or start != 0
+    stop = n if stop is None else stop
+    sd = np.float32(std)
+    v = _draw("normal", seed, name, start, stop, dtype=np.uint16, post=lambda v: f32_to_bf16_bits(v * sd))
     return v if sub else v.reshape(shape)
 
 
@@ -227,6 +245,13 @@ class SyntheticModel:
             return _round_like(v, c.bf16)
         return normal(c.seed, name, shp, c.weight_std, c.bf16)
 
+    def bits(self, kind: str, layer: Optional[int] = None) -> np.ndarray:
+        """bf16 bit patterns (uint16) of ``get(kind, layer)`` for a bf16 configuration."""
+        c = self.cfg
+        if kind in ("attention_norm", "ffn_norm", "norm"):
+            return f32_to_bf16_bits(self.get(kind, layer))
+        return normal_bits(c.seed, tensor_name(kind, layer), self.shape(kind), c.weight_std)
+
     def rows(self, kind: str, rows: np.ndarray) -> np.ndarray:
         """Selected rows of a [rows, cols] weight (embedding lookups without the full table)."""
         c = self.cfg
@@ -256,6 +281,12 @@ def hidden_x(cfg: Config) -> np.ndarray:
     return normal(cfg.seed, f"x.{cfg.seq_len}", (cfg.batch, cfg.seq_len, cfg.dim), 1.0, cfg.bf16)
 
 
+def kv_cache_bits(cfg: Config, layer: int, which: str) -> np.ndarray:
+    """bf16 bit patterns of the whole seeded cache block of one layer, [batch, cache_len, G, hd]."""
+    shape = (cfg.batch, cfg.cache_len, cfg.n_kv_heads, cfg.head_dim)
+    return normal_bits(cfg.seed, f"cache_{which}.{layer}", shape, 1.0)
+
+
 def kv_cache_block(cfg: Config, layer: int, which: str, b0: int = 0, b1: Optional[int] = None) -> np.ndarray:
     """Seeded KV-cache contents ~ N(0, 1) for sequences [b0, b1) of one layer.
 
@@ -271,6 +302,6 @@ def kv_cache_block(cfg: Config, layer: int, which: str, b0: int = 0, b1: Optiona
 
 __all__ = [
     "CHUNK", "Config", "CONFIGS", "SyntheticModel", "LAYER_TENSORS", "tensor_name",
-    "f32_to_bf16_bits", "bf16_bits_to_f32", "normal", "token_ids", "prompt_ids", "hidden_x",
-    "kv_cache_block",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "normal", "normal_bits", "token_ids", "prompt_ids", "hidden_x",
+    "kv_cache_block", "kv_cache_bits",
 ]

@@ -54,3 +54,14 @@ def test_kv_cache_block_slices():
     full = I.kv_cache_block(cfg, 0, "k")
     assert full.shape == (3, 16, 2, 16)
     assert np.array_equal(I.kv_cache_block(cfg, 0, "k", 1, 2)[0], full[1])
+
+
+def test_bits_match_values():
+    cfg = I.CONFIGS["c2"].with_(dim=128, n_heads=2, n_kv_heads=1, vocab_size=300)
+    m = I.SyntheticModel(cfg, 256)
+    assert np.array_equal(I.bf16_bits_to_f32(m.bits("wq", 0)), m.get("wq", 0))
+    n = I.CHUNK + 77
+    bits = I.normal_bits(4, "t", (n,), 0.5)
+    assert np.array_equal(I.bf16_bits_to_f32(bits), I.normal(4, "t", (n,), 0.5, True))
+    c5 = I.CONFIGS["c5"].with_(batch=2, cache_len=8, n_kv_heads=2, dim=128, n_heads=2)
+    assert np.array_equal(I.bf16_bits_to_f32(I.kv_cache_bits(c5, 1, "v")), I.kv_cache_block(c5, 1, "v"))
