@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecodeAttnArgs a) {
       const float kv = Elem<TC>::load(kr + d);
       for (int r = 0; r < n_rep; ++r) dot[r] = fmaf(qs[r][d], kv, dot[r]);
     }
-    for (int r = 0; r < n_rep; ++r) sc[r][tid] = dot[r] * a.scale;
+    for (int r = 0; r < n_rep; ++r) sc[r][tid] = dot[r] * a.scale * kLog2e;
   }
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63;
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecodeAttnArgs a) {
     mx = wave_max(mx);
     float sum = 0.f;
     for (int j = lane; j < nk; j += 64) {
-      const float p = expf(sc[r][j] - mx);
+      const float p = exp2f(sc[r][j] - mx);
       sc[r][j] = p;
       sum += p;
     }
@@ -311,8 +311,186 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecodeAttnArgs a) {
   }
 }
 
-// Combine the chunk partials of one (sequence, head):
-// O = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c, M = max_c m_c.
+// ---------------------------------------------------------------------------
+// Decode, bf16 cache, MFMA for the scores.  A block takes 256 keys of one
+// (sequence, KV group); each wave takes 64 of them.
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16: the K rows are the A operand,
+//   read straight from the cache (16 keys x 64 contiguous bytes per load);
+//   the group's n_rep query heads are the B columns, each fp32 query split
+//   into hi + lo bf16 (two MFMAs) so the scores keep ~16 significant bits.
+//   P V runs on the vector ALUs in fp32: lane (kq, dc) streams 16-byte
+//   pieces of the V rows of keys 4i + kq, reads the probabilities of that
+//   key from LDS and accumulates 8 output columns for every head.
+// The four waves are merged through LDS into one (max, sum, output) partial
+// per head and key chunk; maxima are in log2 units.
+// ---------------------------------------------------------------------------
+template <int HD, int NR>
+__global__ __launch_bounds__(256) void attn_decode_mfma(DecodeAttnArgs a) {
+  constexpr int CH = 256;
+  constexpr int KW = 64;
+  constexpr int NS = HD / 32;
+  constexpr int NDC = HD / 8;
+  __shared__ __align__(16) float Ps[4][KW][NR];
+  __shared__ float red_m[4][NR], red_l[4][NR];
+  __shared__ __align__(16) float red_o[4][NR][HD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ci = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int n_rep = a.H / a.G;
+  int pb = a.pos[b];
+  pb = pb < 0 ? 0 : (pb > a.cap - 1 ? a.cap - 1 : pb);
+  const int c0 = ci * CH;
+  const int kend = min(c0 + CH, pb + 1);
+  const int64_t pidx = ((int64_t)b * a.H + g * n_rep) * a.nchunk + ci;
+  if (c0 >= kend) {
+    for (int i = tid; i < n_rep * HD; i += 256) a.po[(pidx + (int64_t)(i / HD) * a.nchunk) * HD + i % HD] = 0.f;
+    if (tid < n_rep) {
+      a.pm[pidx + (int64_t)tid * a.nchunk] = -INFINITY;
+      a.pl[pidx + (int64_t)tid * a.nchunk] = 0.f;
+    }
+    return;
+  }
+  const int j = lane & 15, grp = lane >> 4;
+  const int64_t kstride = (int64_t)a.G * HD;
+  const u16 *Kb = static_cast<const u16 *>(a.k) + ((int64_t)b * a.cap * a.G + g) * HD;
+  const u16 *Vb = static_cast<const u16 *>(a.v) + ((int64_t)b * a.cap * a.G + g) * HD;
+  const int kw0 = c0 + wave * KW;
+
+  // issue every load of this wave first: K fragments and V pieces
+  uint4 kf[4][NS];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int key = kw0 + kb * 16 + j;
+    const bool ok = key < kend;
+    const u16 *src = Kb + (int64_t)(ok ? key : 0) * kstride + grp * 8;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) kf[kb][t] = ok ? *reinterpret_cast<const uint4 *>(src + t * 32) : make_uint4(0, 0, 0, 0);
+  }
+  uint4 vf[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int key = kw0 + i * 4 + grp;
+    const bool ok = key < kend && j < NDC;
+    vf[i] = ok ? *reinterpret_cast<const uint4 *>(Vb + (int64_t)key * kstride + j * 8) : make_uint4(0, 0, 0, 0);
+  }
+
+  // query fragments (B operand): column j = head of the group, k = head_dim
+  const float c = a.scale * kLog2e;
+  bf16x8 qh[NS], ql[NS];
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = 0.f;
+      if (j < n_rep) v = a.q[((int64_t)b * a.H + g * n_rep + j) * HD + t * 32 + grp * 8 + e] * c;
+      u16 hi, lo;
+      split_hilo(v, hi, lo);
+      qh[t][e] = __builtin_bit_cast(__bf16, hi);
+      ql[t][e] = __builtin_bit_cast(__bf16, lo);
+    }
+  }
+
+  // scores (log2 units), masked beyond the sequence's position
+  f32x4 sc[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, kf[kb][t]);
+      sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh[t], sc[kb], 0, 0, 0);
+      sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql[t], sc[kb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = kw0 + kb * 16 + 4 * grp + r;
+      if (key >= kend) sc[kb][r] = -INFINITY;
+      mx = fmaxf(mx, sc[kb][r]);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  float ls = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = mx == -INFINITY ? 0.f : exp2f(sc[kb][r] - mx);
+      ls += p;
+      if (j < NR) Ps[wave][kb * 16 + 4 * grp + r][j] = p;
+    }
+  ls += __shfl_xor(ls, 16, kWave);
+  ls += __shfl_xor(ls, 32, kWave);
+  if (grp == 0 && j < NR) {
+    red_m[wave][j] = mx;
+    red_l[wave][j] = ls;
+  }
+  __syncthreads();
+
+  // P V in fp32: lane (grp, j) handles keys 4i + grp and columns 8j .. 8j+7
+  float acc[NR][8];
+#pragma unroll
+  for (int h = 0; h < NR; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int kl = i * 4 + grp;
+    float v[8];
+    const u16 *vp = reinterpret_cast<const u16 *>(&vf[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = bf2f(vp[e]);
+#pragma unroll
+    for (int h4 = 0; h4 < NR; h4 += 4) {
+      const float4 p4 = *reinterpret_cast<const float4 *>(&Ps[wave][kl][h4]);
+      const float pp[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h4 + hh][e] = fmaf(pp[hh], v[e], acc[h4 + hh][e]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < NR; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float t = acc[h][e];
+      t += __shfl_xor(t, 16, kWave);
+      t += __shfl_xor(t, 32, kWave);
+      acc[h][e] = t;
+    }
+  if (grp == 0 && j < NDC) {
+#pragma unroll
+    for (int h = 0; h < NR; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_o[wave][h][j * 8 + e] = acc[h][e];
+  }
+  __syncthreads();
+
+  // merge the four waves into this chunk's partial
+  for (int i = tid; i < n_rep * HD; i += 256) {
+    const int h = i / HD, d = i % HD;
+    float M = red_m[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = red_m[w][h] == -INFINITY ? 0.f : exp2f(red_m[w][h] - M);
+      L += wt * red_l[w][h];
+      O += wt * red_o[w][h][d];
+    }
+    a.po[(pidx + (int64_t)h * a.nchunk) * HD + d] = O;
+    if (d == 0) {
+      a.pm[pidx + (int64_t)h * a.nchunk] = M;
+      a.pl[pidx + (int64_t)h * a.nchunk] = L;
+    }
+  }
+}
+
+// Combine the chunk partials of one (sequence, head); maxima are in log2
+// units: O = sum_c 2^{m_c - M} o_c / sum_c 2^{m_c - M} l_c, M = max_c m_c.
 template <int HD>
 __global__ __launch_bounds__(HD) void attn_combine_kernel(DecodeAttnArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
@@ -323,7 +501,7 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(DecodeAttnArgs a) {
   for (int c = 0; c < a.nchunk; ++c) {
     const float mc = a.pm[base + c];
     if (mc == -INFINITY) continue;
-    const float w = expf(mc - M);
+    const float w = exp2f(mc - M);
     L += w * a.pl[base + c];
     acc += w * a.po[(base + c) * HD + d];
   }
@@ -355,7 +533,12 @@ hipError_t prefill_hd(int dtype, const AttnArgs &a, hipStream_t s) {
 template <int HD>
 hipError_t decode_hd(int dtype, const DecodeAttnArgs &a, hipStream_t s) {
   dim3 grid(a.nchunk, a.G, a.B);
-  if (dtype == 1)
+  const int n_rep = a.H / a.G;
+  if (dtype == 1 && n_rep <= 4)
+    hipLaunchKernelGGL((attn_decode_mfma<HD, 4>), grid, dim3(256), 0, s, a);
+  else if (dtype == 1 && n_rep <= 8)
+    hipLaunchKernelGGL((attn_decode_mfma<HD, 8>), grid, dim3(256), 0, s, a);
+  else if (dtype == 1)
     hipLaunchKernelGGL((attn_decode_kernel<u16, HD>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((attn_decode_kernel<float, HD>), grid, dim3(256), 0, s, a);

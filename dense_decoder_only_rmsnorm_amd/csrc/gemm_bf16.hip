@@ -9,14 +9,20 @@
 //
 // Tiling: a block of 256 threads (4 waves in a 2x2 grid) owns a BM x BN
 // output tile; each wave owns (BM/2) x (BN/2) as 32x32 MFMA blocks.  The K
-// loop steps by 64: the next A/B tiles are fetched into registers with 16-byte
-// loads while the MFMAs consume the current LDS buffer, then written to the
-// other buffer.  LDS rows are padded by 16 bytes so the 16-byte fragment reads
-// of 32 consecutive rows spread over all banks.
+// loop steps by 64 through two LDS stages.  Tiles move global -> LDS with
+// global_load_lds_dwordx4 (no staging registers): one wave instruction fills
+// 1 KB = 8 tile rows of 128 bytes, lane L landing at 16-byte slot L.  Each
+// lane fetches the global piece that belongs in its slot under an XOR
+// swizzle (16-byte chunk c of row r lives at chunk c ^ ((r >> 1) & 7)), so
+// the 16-byte fragment reads of 16 consecutive rows hit 16 distinct bank
+// groups.  The next stage is loading while the MFMAs consume the current
+// one; operand fragments are double-buffered in registers across k-steps.
 //
 // MFMA 32x32x16 operand layout (lane l): A supplies row (l % 32) and eight
 // consecutive k at 8*(l / 32); B likewise for output column (l % 32).  Output
 // register r of lane l holds row 8*(r/4) + 4*(l/32) + (r%4), column l % 32.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -24,22 +30,16 @@ namespace llk {
 
 namespace {
 constexpr int BK = 64;
-constexpr int PADK = 8;
-constexpr int LDK = BK + PADK;  // bf16 elements per LDS row
-
-struct Chunk16 {
-  uint4 v;
-};
 
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int ACH = BM * (BK / 8) / 256;  // 16-byte chunks per thread (A)
-  constexpr int BCH = BN * (BK / 8) / 256;
+  constexpr int RS = BK;                  // LDS row stride (bf16), 128 bytes, unpadded
+  constexpr int AI = BM / 32, BI = BN / 32;  // 8-row load instructions per wave (A, B)
   extern __shared__ __align__(16) u16 smem[];
-  u16 *As = smem;                      // [2][BM][LDK]
-  u16 *Bs = smem + 2 * BM * LDK;       // [2][BN][LDK]
+  u16 *As = smem;                         // [2][BM][RS]
+  u16 *Bs = smem + 2 * BM * RS;           // [2][BN][RS]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -48,62 +48,55 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const int n0 = blockIdx.y * BN;
   const int K = a.K;
 
-  // global source rows for this thread's chunks
-  const u16 *asrc[ACH];
-  bool aok[ACH];
-  int acol[ACH], arow[ACH];
+  // Loader: wave w fills tile rows 8j..8j+7 for j = w*AI + i (A) and w*BI + i
+  // (B).  Lane L writes slot L of that 1 KB block: row 8j + L/8, physical
+  // chunk L%8, which holds logical chunk (L%8) ^ ((row >> 1) & 7).  Rows past
+  // M (A) or past the weight's rows (B) read a clamped valid row: they only
+  // feed outputs that are never stored.
+  const int lr = lane >> 3, lq = lane & 7;
+  const u16 *asrc[AI];
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int c = tid + i * 256;
-    arow[i] = c / (BK / 8);
-    acol[i] = (c % (BK / 8)) * 8;
-    const int gr = m0 + arow[i];
-    aok[i] = gr < a.M;
-    asrc[i] = a.A + (int64_t)(aok[i] ? gr : 0) * a.lda + acol[i];
+  for (int i = 0; i < AI; ++i) {
+    const int t = (wave * AI + i) * 8 + lr;
+    const int c = lq ^ ((t >> 1) & 7);
+    asrc[i] = a.A + (int64_t)min(m0 + t, a.M - 1) * a.lda + c * 8;
   }
-  const u16 *bsrc[BCH];
-  bool bok[BCH];
-  int bcol[BCH], brow[BCH];
+  const u16 *bsrc[BI];
 #pragma unroll
-  for (int i = 0; i < BCH; ++i) {
-    const int c = tid + i * 256;
-    brow[i] = c / (BK / 8);
-    bcol[i] = (c % (BK / 8)) * 8;
-    const int t = brow[i];
+  for (int i = 0; i < BI; ++i) {
+    const int t = (wave * BI + i) * 8 + lr;
+    const int c = lq ^ ((t >> 1) & 7);
     const u16 *base;
-    int wr;
-    bool ok;
+    int wr, nrows;
     if (EPI == EPI_SWIGLU) {
-      const int F = a.N / 2;
-      wr = n0 / 2 + (t >> 6) * 32 + (t & 31);
+      wr = n0 / 2 + (t >> 6) * 32 + (t & 31);  // 64 tile rows = 32 gate rows (w1) + 32 up rows (w3)
       base = ((t >> 5) & 1) ? a.B1 : a.B0;
-      ok = wr < F;
+      nrows = a.N / 2;
     } else if (EPI == EPI_QKV_ROPE) {
       const int n = n0 + t;
-      ok = n < a.N;
       base = n < a.nq ? a.B0 : (n < a.nq + a.nk ? a.B1 : a.B2);
       wr = n < a.nq ? n : (n < a.nq + a.nk ? n - a.nq : n - a.nq - a.nk);
+      nrows = n < a.nq ? a.nq : (n < a.nq + a.nk ? a.nk : a.N - a.nq - a.nk);
     } else {
       wr = n0 + t;
       base = a.B0;
-      ok = wr < a.N;
+      nrows = a.N;
     }
-    bok[i] = ok;
-    bsrc[i] = base + (int64_t)(ok ? wr : 0) * a.ldb + bcol[i];
+    bsrc[i] = base + (int64_t)min(wr, nrows - 1) * a.ldb + c * 8;
   }
-
-  uint4 ra[ACH], rb[BCH];
-  auto gload = [&](int k0) {
+  auto issue = [&](int stage, int k0) {
+    u16 *ad = As + stage * BM * RS;
+    u16 *bd = Bs + stage * BN * RS;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) ra[i] = aok[i] ? *reinterpret_cast<const uint4 *>(asrc[i] + k0) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < AI; ++i) {
+      const int j = __builtin_amdgcn_readfirstlane(wave * AI + i);
+      __builtin_amdgcn_global_load_lds((const void *)(asrc[i] + k0), (__attribute__((address_space(3))) void *)(ad + j * 8 * RS), 16, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) rb[i] = bok[i] ? *reinterpret_cast<const uint4 *>(bsrc[i] + k0) : make_uint4(0, 0, 0, 0);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) *reinterpret_cast<uint4 *>(As + (buf * BM + arow[i]) * LDK + acol[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) *reinterpret_cast<uint4 *>(Bs + (buf * BN + brow[i]) * LDK + bcol[i]) = rb[i];
+    for (int i = 0; i < BI; ++i) {
+      const int j = __builtin_amdgcn_readfirstlane(wave * BI + i);
+      __builtin_amdgcn_global_load_lds((const void *)(bsrc[i] + k0), (__attribute__((address_space(3))) void *)(bd + j * 8 * RS), 16, 0, 0);
+    }
   };
 
   f32x16 acc[FM][FN];
@@ -114,98 +107,147 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // fragment read offsets: row (lane & 31) of a 32-row block, logical chunk
+  // 2*kk + (lane >> 5), swizzled with ((row >> 1) & 7)
+  const int frow = lane & 31;
+  const int sw = (frow >> 1) & 7;
+  int koff[BK / 16];
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) koff[kk] = (((2 * kk + (lane >> 5)) ^ sw) * 8);
+
   const int KT = K / BK;
-  gload(0);
-  lstore(0);
+  issue(0, 0);
   __syncthreads();
-  const int lrow = lane & 31, lk = (lane >> 5) * 8;
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const u16 *Ab = As + (buf * BM + wm * WM + lrow) * LDK + lk;
-    const u16 *Bb = Bs + (buf * BN + wn * WN + lrow) * LDK + lk;
+    const int cur = kt & 1;
+    if (kt + 1 < KT) issue(cur ^ 1, (kt + 1) * BK);
+    const u16 *Ab = As + (cur * BM + wm * WM + frow) * RS;
+    const u16 *Bb = Bs + (cur * BN + wn * WN + frow) * RS;
+    bf16x8 af[2][FM], bfr[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[0][i] = *reinterpret_cast<const bf16x8 *>(Ab + i * 32 * RS + koff[0]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8 *>(Bb + j * 32 * RS + koff[0]);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[FM], bfr[FN];
+      const int cb = kk & 1;
+      if (kk + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8 *>(Ab + i * 32 * LDK + kk * 16);
+        for (int i = 0; i < FM; ++i)
+          af[cb ^ 1][i] = *reinterpret_cast<const bf16x8 *>(Ab + i * 32 * RS + koff[kk + 1]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8 *>(Bb + j * 32 * LDK + kk * 16);
+        for (int j = 0; j < FN; ++j)
+          bfr[cb ^ 1][j] = *reinterpret_cast<const bf16x8 *>(Bb + j * 32 * RS + koff[kk + 1]);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) lstore(buf ^ 1);
-    __syncthreads();
+    __syncthreads();  // the next stage has landed (waits for this wave's loads) and this one is free
   }
 
   // ---------------- epilogue ----------------
   const int col_l = lane & 31;
-  const int rbase = m0 + wm * WM + 4 * (lane >> 5);
+  const int rloc = wm * WM + 4 * (lane >> 5);  // tile-local row base of this lane
+  if (EPI == EPI_RESID || EPI == EPI_STORE_F32) {
+    // fp32 outputs: each store instruction writes 32 consecutive floats of a row
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * WN + j * 32 + col_l;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + rloc + i * 32 + 8 * (r / 4) + (r % 4);
+          if (row < a.M && col < a.N) {
+            const float v = acc[i][j][r];
+            float *C = static_cast<float *>(a.C);
+            if (EPI == EPI_RESID)
+              C[(int64_t)row * a.ldc + col] = a.R[(int64_t)row * a.ldr + col] + v;
+            else
+              C[(int64_t)row * a.ldc + col] = v;
+          }
+        }
+      }
+    return;
+  }
+
+  // bf16 outputs: finish the values in registers, stage the tile in LDS as
+  // bf16, then write it out in 16-byte pieces of 8 consecutive columns.
+  constexpr int CN = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
+  constexpr int LDC = CN + 8;
+  u16 *Cs = smem;  // [BM][LDC], reuses the operand buffers (loop ended with a barrier)
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * WN + j * 32 + col_l;
       if (EPI == EPI_SWIGLU) {
-        if (j & 1) continue;  // odd blocks (up) are consumed with their gate block
-        const int ucol = n0 / 2 + (wn * WN / 64 + j / 2) * 32 + col_l;
-        const int F = a.N / 2;
+        if (j & 1) continue;  // the up block j+1 is consumed with its gate block j
+        const int ccol = (wn * WN / 64 + j / 2) * 32 + col_l;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = rbase + i * 32 + 8 * (r / 4) + (r % 4);
-          if (row < a.M && ucol < F) {
-            const float g = acc[i][j][r], up = acc[i][j + 1][r];
-            static_cast<u16 *>(a.C)[(int64_t)row * a.ldc + ucol] = f2bf(silu(g) * up);
-          }
-        }
-      } else if (EPI == EPI_QKV_ROPE) {
-        const int Hq = a.H * a.hd, Hk = a.G * a.hd;
-        const bool rot = col < Hq + Hk;
-        const int c = col < Hq ? col : (col < Hq + Hk ? col - Hq : col - Hq - Hk);
-        const int d = c % a.hd;
-        const bool odd = col & 1;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + i * 32 + 8 * (r / 4) + (r % 4);
-          float v = acc[i][j][r];
-          const float pv = __shfl_xor(v, 1, kWave);
-          const int rr = row < a.M ? row : a.M - 1;
-          const int b = rr / a.S, s = rr % a.S;
-          if (rot) {
-            const float2 cs = a.tab[(int64_t)s * (a.hd / 2) + d / 2];
-            const float2 y = odd ? rotate_pair(pv, v, cs.x, cs.y) : rotate_pair(v, pv, cs.x, cs.y);
-            v = odd ? y.y : y.x;
-          }
-          if (row < a.M && col < a.N) {
-            if (col < Hq) {
-              a.q[(int64_t)row * Hq + col] = f2bf(v);
-            } else {
-              const int g = c / a.hd;
-              const int p = a.start_pos + s;
-              u16 *dst = static_cast<u16 *>(col < Hq + Hk ? a.kc : a.vc);
-              dst[(((int64_t)b * a.cap + p) * a.G + g) * a.hd + d] = f2bf(v);
-            }
-          }
+          const int rr = rloc + i * 32 + 8 * (r / 4) + (r % 4);
+          Cs[rr * LDC + ccol] = f2bf(silu(acc[i][j][r]) * acc[i][j + 1][r]);
         }
       } else {
+        const int ccol = wn * WN + j * 32 + col_l;
+        if (EPI == EPI_QKV_ROPE) {
+          const int col = n0 + ccol;
+          const int Hq = a.H * a.hd, Hk = a.G * a.hd;
+          const bool rot = col < Hq + Hk;
+          const int d = (col < Hq ? col : col - Hq) % a.hd;
+          const bool odd = col & 1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + i * 32 + 8 * (r / 4) + (r % 4);
-          if (row < a.M && col < a.N) {
-            const float v = acc[i][j][r];
-            if (EPI == EPI_RESID) {
-              float *C = static_cast<float *>(a.C);
-              C[(int64_t)row * a.ldc + col] = a.R[(int64_t)row * a.ldr + col] + v;
-            } else if (EPI == EPI_STORE_F32) {
-              static_cast<float *>(a.C)[(int64_t)row * a.ldc + col] = v;
-            } else {
-              static_cast<u16 *>(a.C)[(int64_t)row * a.ldc + col] = f2bf(v);
+          for (int r = 0; r < 16; ++r) {
+            const int rr = rloc + i * 32 + 8 * (r / 4) + (r % 4);
+            float v = acc[i][j][r];
+            const float pv = __shfl_xor(v, 1, kWave);
+            if (rot) {
+              const int row = min(m0 + rr, a.M - 1);
+              const float2 cs = a.tab[(int64_t)(row % a.S) * (a.hd / 2) + d / 2];
+              v = odd ? pv * cs.y + v * cs.x : v * cs.x - pv * cs.y;
             }
+            Cs[rr * LDC + ccol] = f2bf(v);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rr = rloc + i * 32 + 8 * (r / 4) + (r % 4);
+            Cs[rr * LDC + ccol] = f2bf(acc[i][j][r]);
           }
         }
       }
+    }
+  }
+  __syncthreads();
+  constexpr int CPR = CN / 8;  // 16-byte pieces per tile row
+  for (int c = tid; c < BM * CPR; c += 256) {
+    const int rr = c / CPR, c8 = (c % CPR) * 8;
+    const int row = m0 + rr;
+    if (row >= a.M) continue;
+    const uint4 val = *reinterpret_cast<const uint4 *>(Cs + rr * LDC + c8);
+    if (EPI == EPI_SWIGLU) {
+      const int ucol = n0 / 2 + c8;
+      if (ucol < a.N / 2) *reinterpret_cast<uint4 *>(static_cast<u16 *>(a.C) + (int64_t)row * a.ldc + ucol) = val;
+    } else if (EPI == EPI_QKV_ROPE) {
+      const int col = n0 + c8;
+      if (col >= a.N) continue;
+      const int Hq = a.H * a.hd, Hk = a.G * a.hd;
+      if (col < Hq) {
+        *reinterpret_cast<uint4 *>(a.q + (int64_t)row * Hq + col) = val;
+      } else {
+        const bool isk = col < Hq + Hk;
+        const int cc = isk ? col - Hq : col - Hq - Hk;
+        const int g = cc / a.hd, d = cc % a.hd;
+        const int b = row / a.S, p = a.start_pos + row % a.S;
+        u16 *dst = static_cast<u16 *>(isk ? a.kc : a.vc);
+        *reinterpret_cast<uint4 *>(dst + (((int64_t)b * a.cap + p) * a.G + g) * a.hd + d) = val;
+      }
+    } else {
+      const int col = n0 + c8;
+      if (col < a.N) *reinterpret_cast<uint4 *>(static_cast<u16 *>(a.C) + (int64_t)row * a.ldc + col) = val;
     }
   }
 }
@@ -213,7 +255,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 template <int BM, int BN, int EPI>
 hipError_t launch_tile(const GemmArgs &a, hipStream_t s) {
   dim3 grid((a.M + BM - 1) / BM, (a.N + BN - 1) / BN);  // a.N counts B-rows
-  const size_t lds = (size_t)2 * (BM + BN) * LDK * sizeof(u16);
+  constexpr int CN = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  const size_t lds = std::max((size_t)2 * (BM + BN) * BK * sizeof(u16), (size_t)BM * (CN + 8) * sizeof(u16));
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, EPI>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   (void)attr;
