@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run one workload only (profiling); the JSON line then omits the other")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -160,6 +162,13 @@ def main():
     from dense_decoder_only_rmsnorm_amd import runtime as R
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy of 1 GiB done")
     c4, c5 = I.CONFIGS["c4"], I.CONFIGS["c5"]
     t0 = time.time()
     log("generating and uploading the 8B-shaped weights (seed of the prefill configuration) ...")

@@ -243,6 +243,7 @@ struct DecodeWs {
   void *xn;         // bf16 hi/lo [2][B][D] or fp32 [B][D]
   float *qkv_part;  // bf16: [ks1][B][Nqkv]; fp32: [B][Nqkv]
   float *q;         // [B][Hq]
+  u16 *qhl;         // bf16 path: [2][B][Hq] (q scaled into log2 units)
   float *pm, *pl, *po;
   void *o;          // bf16 hi/lo [2][B][Hq] or fp32 [B][Hq]
   float *wo_part;   // [ks2][B][D]
@@ -262,6 +263,7 @@ DecodeWs carve_decode(Carver &c, const Dims &d, int B, int cap) {
   w.h = c.take<float>(Bz * d.D);
   w.tab = c.take<float2>(Bz * (d.hd / 2));
   w.q = c.take<float>(Bz * d.Hq());
+  w.qhl = c.take<u16>(2 * Bz * d.Hq());
   w.pm = c.take<float>(Bz * d.H * w.nchunk);
   w.pl = c.take<float>(Bz * d.H * w.nchunk);
   w.po = c.take<float>(Bz * d.H * w.nchunk * d.hd);
@@ -674,12 +676,15 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
     ra.start_pos = 0;
     ra.cap = cap;
     ra.qout = dw.q;
+    ra.qhl = bf ? dw.qhl : nullptr;
+    ra.qscale = (float)(1.4426950408889634 / sqrt((double)d.hd));
     ra.kc = kv[l].k;
     ra.vc = kv[l].v;
     LAUNCH("rope_qkv", launch_rope_qkv(d.dt, ra, s));
     // a7: attention over the cache
     DecodeAttnArgs da{};
     da.q = dw.q;
+    da.qhl = bf ? dw.qhl : nullptr;
     da.k = kv[l].k;
     da.v = kv[l].v;
     da.pos = pos;

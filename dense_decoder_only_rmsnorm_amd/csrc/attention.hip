@@ -489,6 +489,195 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(DecodeAttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode, bf16 cache, head_dim 128: scores and P V both on MFMA
+// (v_mfma_f32_16x16x32_bf16).  A block takes 256 keys of one (sequence, KV
+// group), each wave 64 of them.
+//   * K rows are loaded straight into registers as the A operand of
+//     S^T = K Q^T (16 keys x 64 contiguous bytes per load); the query heads
+//     of the group are the B columns, pre-split into hi + lo bf16 and
+//     pre-scaled by log2(e)/sqrt(hd) by the RoPE kernel.
+//   * V rows go HBM -> LDS with global_load_lds_dwordx4 (1 KB = 4 rows per
+//     wave instruction, 16-byte chunk c of row r stored at chunk c ^ (r & 15)).
+//   * P stays in registers: the score accumulator layout (lane = head column,
+//     four keys per register group) is already the A-operand layout of
+//     O = P V.  P is split into hi + lo bf16 (two MFMAs against the same V
+//     fragment, ~16 significant bits) and V's B operand is read with
+//     ds_read_b64_tr_b16, which hands lane i of each 16-lane group column i
+//     of the four 32-byte row pieces its group addresses.
+// The four waves merge into one (max, sum, output) partial per head and key
+// chunk; maxima are in log2 units.
+// ---------------------------------------------------------------------------
+template <int NR>
+__global__ __launch_bounds__(256) void attn_decode_mfma2(DecodeAttnArgs a) {
+  constexpr int HD = 128;
+  constexpr int CH = 256;
+  constexpr int KW = 64;
+  constexpr int NS = HD / 32;  // score k-steps
+  constexpr int NB = HD / 16;  // output column blocks
+  __shared__ __align__(16) u16 Vs[4][KW * HD];  // 16 KB per wave
+  __shared__ float red_m[4][NR], red_l[4][NR];
+  __shared__ __align__(16) float red_o[4][NR][HD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ci = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int n_rep = a.H / a.G;
+  int pb = a.pos[b];
+  pb = pb < 0 ? 0 : (pb > a.cap - 1 ? a.cap - 1 : pb);
+  const int c0 = ci * CH;
+  const int kend = min(c0 + CH, pb + 1);
+  const int64_t pidx = ((int64_t)b * a.H + g * n_rep) * a.nchunk + ci;
+  if (c0 >= kend) {
+    for (int i = tid; i < n_rep * HD; i += 256) a.po[(pidx + (int64_t)(i / HD) * a.nchunk) * HD + i % HD] = 0.f;
+    if (tid < n_rep) {
+      a.pm[pidx + (int64_t)tid * a.nchunk] = -INFINITY;
+      a.pl[pidx + (int64_t)tid * a.nchunk] = 0.f;
+    }
+    return;
+  }
+  const int j = lane & 15, grp = lane >> 4;
+  const int64_t kstride = (int64_t)a.G * HD;
+  const u16 *Kb = static_cast<const u16 *>(a.k) + ((int64_t)b * a.cap * a.G + g) * HD;
+  const u16 *Vb = static_cast<const u16 *>(a.v) + ((int64_t)b * a.cap * a.G + g) * HD;
+  const int kw0 = c0 + wave * KW;
+  const int kmax = kend - 1;  // keys past the end read a valid row; their scores are masked
+
+  // V: 16 direct-to-LDS instructions, 4 rows each; lane L -> row 4i + L/16, chunk L%16
+  u16 *vs = Vs[wave];
+#pragma unroll
+  for (int i = 0; i < KW / 4; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    const int key = min(kw0 + r, kmax);
+    __builtin_amdgcn_global_load_lds((const void *)(Vb + (int64_t)key * kstride + c * 8),
+                                     (__attribute__((address_space(3))) void *)(vs + i * 4 * HD), 16, 0, 0);
+  }
+  // K fragments (A operand): key kw0 + 16kb + j, head_dim slice 32t + 8grp
+  uint4 kf[4][NS];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int key = min(kw0 + kb * 16 + j, kmax);
+    const u16 *src = Kb + (int64_t)key * kstride + grp * 8;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) kf[kb][t] = *reinterpret_cast<const uint4 *>(src + t * 32);
+  }
+  // query fragments (B operand): column j = head of the group
+  bf16x8 qh[NS], ql[NS];
+  {
+    const int hq = j < n_rep ? j : 0;
+    const int64_t qo = ((int64_t)b * a.H + g * n_rep + hq) * HD + grp * 8;
+    const int64_t plane = (int64_t)a.B * a.H * HD;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      uint4 h4 = *reinterpret_cast<const uint4 *>(a.qhl + qo + t * 32);
+      uint4 l4 = *reinterpret_cast<const uint4 *>(a.qhl + plane + qo + t * 32);
+      if (j >= n_rep) h4 = l4 = make_uint4(0, 0, 0, 0);
+      qh[t] = __builtin_bit_cast(bf16x8, h4);
+      ql[t] = __builtin_bit_cast(bf16x8, l4);
+    }
+  }
+
+  // S^T (log2 units), masked past the sequence's position
+  f32x4 sc[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, kf[kb][t]);
+      sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh[t], sc[kb], 0, 0, 0);
+      sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql[t], sc[kb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (kw0 + kb * 16 + 4 * grp + r >= kend) sc[kb][r] = -INFINITY;
+      mx = fmaxf(mx, sc[kb][r]);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  float ls = 0.f;
+  bf16x8 pf[2], pl[2];  // A operands (hi, lo) of P V for the two 32-key steps
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = mx == -INFINITY ? 0.f : exp2f(sc[kb][r] - mx);
+      ls += p;
+      const __bf16 ph = (__bf16)p;
+      pf[kb >> 1][(kb & 1) * 4 + r] = ph;
+      pl[kb >> 1][(kb & 1) * 4 + r] = (__bf16)(p - (float)ph);
+    }
+  ls += __shfl_xor(ls, 16, kWave);
+  ls += __shfl_xor(ls, 32, kWave);
+  if (grp == 0 && j < NR) {
+    red_m[wave][j] = mx;
+    red_l[wave][j] = ls;
+  }
+
+  // O = P V: B operand via transposed LDS reads.  For step t, half h, lane
+  // (grp, j) addresses row 32t + 16h + 4grp + j/4, columns 16nb + 4(j%4) .. +3.
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's V rows have landed
+  __builtin_amdgcn_wave_barrier();
+  f32x4 o[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int e = j >> 2, q = j & 3;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      // whole 32-bit words are moved: element-wise bit casts of the read
+      // results are not kept apart by this compiler
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      u32x2 wv[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 32 * t + 16 * h + 4 * grp + e;
+        const int c = (2 * nb + (q >> 1)) ^ (r & 15);
+        const int off = (r * HD + c * 8 + (q & 1) * 4) * (int)sizeof(u16);
+        const v4s w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s *)((__attribute__((address_space(3))) char *)vs + off));
+        wv[h] = __builtin_bit_cast(u32x2, w);
+      }
+      const uint4 vw = make_uint4(wv[0].x, wv[0].y, wv[1].x, wv[1].y);
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, vw);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[t], vb, o[nb], 0, 0, 0);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[t], vb, o[nb], 0, 0, 0);
+    }
+  }
+  // lane (grp, j) holds O[head 4grp + r][16nb + j]
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * grp + r;
+      if (h < NR) red_o[wave][h][nb * 16 + j] = o[nb][r];
+    }
+  __syncthreads();
+
+  for (int i = tid; i < n_rep * HD; i += 256) {
+    const int h = i / HD, d = i % HD;
+    float M = red_m[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = red_m[w][h] == -INFINITY ? 0.f : exp2f(red_m[w][h] - M);
+      L += wt * red_l[w][h];
+      O += wt * red_o[w][h][d];
+    }
+    a.po[(pidx + (int64_t)h * a.nchunk) * HD + d] = O;
+    if (d == 0) {
+      a.pm[pidx + (int64_t)h * a.nchunk] = M;
+      a.pl[pidx + (int64_t)h * a.nchunk] = L;
+    }
+  }
+}
+
 // Combine the chunk partials of one (sequence, head); maxima are in log2
 // units: O = sum_c 2^{m_c - M} o_c / sum_c 2^{m_c - M} l_c, M = max_c m_c.
 template <int HD>
@@ -534,7 +723,11 @@ template <int HD>
 hipError_t decode_hd(int dtype, const DecodeAttnArgs &a, hipStream_t s) {
   dim3 grid(a.nchunk, a.G, a.B);
   const int n_rep = a.H / a.G;
-  if (dtype == 1 && n_rep <= 4)
+  if (dtype == 1 && HD == 128 && a.qhl && n_rep <= 4)
+    hipLaunchKernelGGL((attn_decode_mfma2<4>), grid, dim3(256), 0, s, a);
+  else if (dtype == 1 && HD == 128 && a.qhl && n_rep <= 16)
+    hipLaunchKernelGGL((attn_decode_mfma2<16>), grid, dim3(256), 0, s, a);
+  else if (dtype == 1 && n_rep <= 4)
     hipLaunchKernelGGL((attn_decode_mfma<HD, 4>), grid, dim3(256), 0, s, a);
   else if (dtype == 1 && n_rep <= 8)
     hipLaunchKernelGGL((attn_decode_mfma<HD, 8>), grid, dim3(256), 0, s, a);

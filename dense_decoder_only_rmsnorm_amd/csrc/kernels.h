@@ -30,7 +30,9 @@ struct RopeQkvArgs {
   const int32_t *pos;  // per-sequence start positions or nullptr
   int start_pos;
   int cap;             // cache capacity (positions per sequence)
-  float *qout;         // [rows][H*hd] fp32
+  float *qout;         // [rows][H*hd] fp32 (or nullptr)
+  uint16_t *qhl;       // optional: q * qscale as bf16 hi/lo planes [2][rows][H*hd]
+  float qscale;
   void *kc, *vc;       // [B][cap][G][hd] (dtype)
 };
 
@@ -83,6 +85,7 @@ struct AttnArgs {
 // Decode attention over the cache (split over key chunks, then combined).
 struct DecodeAttnArgs {
   const float *q;                         // [B][H*hd] fp32 (rotated)
+  const uint16_t *qhl;                    // q * scale * log2(e) as bf16 hi/lo planes [2][B][H*hd] (bf16 path)
   const void *k; const void *v;           // [B][cap][G][hd] (dtype)
   const int32_t *pos;                     // [B] query positions (inclusive key range 0..pos)
   int cap, B, H, G, hd, chunk, nchunk;

@@ -45,11 +45,13 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
 //   x[r] += sum_s part[s][r]   (written back to x).
 // w == nullptr skips the normalisation (pure conversion of x).
 // Output modes: 0 fp32, 1 bf16, 2 bf16 hi/lo planes (hi at out, lo at
-// out + out_plane).  One block of 256 threads per row; D <= 8192.
+// out + out_plane).  One block of NT threads per row; D <= 8192.  Few rows
+// (decode) use NT = 1024 so that the partial planes stream with enough
+// loads in flight.
 // ---------------------------------------------------------------------------
-template <typename TW, int MODE>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
-  constexpr int MAXV = 8;
+template <typename TW, int MODE, int NT>
+__global__ __launch_bounds__(NT) void rmsnorm_kernel(NormArgs a) {
+  constexpr int MAXV = 8192 / (NT * 4);
   const int r = blockIdx.x;
   const int D = a.D;
   float *x = a.h + a.in_offset + (int64_t)r * a.in_stride;
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
-    const int i = (j * 256 + threadIdx.x) * 4;
+    const int i = (j * NT + threadIdx.x) * 4;
     if (i < D) {
       float4 t = *reinterpret_cast<const float4 *>(x + i);
       if (a.nsplit > 0) {
@@ -73,17 +75,19 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
   }
   float scale = 1.f;
   if (a.w != nullptr) {
-    __shared__ float red[4];
+    __shared__ float red[NT / 64];
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    const float tot = red[0] + red[1] + red[2] + red[3];
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) tot += red[w];
     scale = 1.0f / sqrtf(tot / (float)D + a.eps);
   }
   const TW *w = static_cast<const TW *>(a.w);
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
-    const int i = (j * 256 + threadIdx.x) * 4;
+    const int i = (j * NT + threadIdx.x) * 4;
     if (i < D) {
       float y[4] = {v[j].x * scale, v[j].y * scale, v[j].z * scale, v[j].w * scale};
       if (w != nullptr) {
@@ -176,7 +180,15 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(RopeQkvArgs a) {
     x1 = y.y;
   }
   if (j < Hq) {
-    *reinterpret_cast<float2 *>(a.qout + (int64_t)r * Hq + j) = make_float2(x0, x1);
+    if (a.qout) *reinterpret_cast<float2 *>(a.qout + (int64_t)r * Hq + j) = make_float2(x0, x1);
+    if (a.qhl) {
+      u16 h0, l0, h1, l1;
+      split_hilo(x0 * a.qscale, h0, l0);
+      split_hilo(x1 * a.qscale, h1, l1);
+      const int64_t o = (int64_t)r * Hq + j;
+      *reinterpret_cast<uint32_t *>(a.qhl + o) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      *reinterpret_cast<uint32_t *>(a.qhl + (int64_t)a.rows * Hq + o) = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
   } else {
     const bool isk = j < Hq + Hk;
     const int c = isk ? j - Hq : j - Hq - Hk;
@@ -276,7 +288,13 @@ hipError_t launch_embed(int dtype, const int32_t *ids, const void *E, float *h, 
 }
 
 hipError_t launch_rmsnorm(int dtype, int mode, const NormArgs &a, int rows, hipStream_t s) {
-#define LLK_NORM(TW, M) hipLaunchKernelGGL((rmsnorm_kernel<TW, M>), dim3(rows), dim3(256), 0, s, a)
+#define LLK_NORM(TW, M)                                                                           \
+  do {                                                                                            \
+    if (rows < 512)                                                                               \
+      hipLaunchKernelGGL((rmsnorm_kernel<TW, M, 1024>), dim3(rows), dim3(1024), 0, s, a);        \
+    else                                                                                          \
+      hipLaunchKernelGGL((rmsnorm_kernel<TW, M, 256>), dim3(rows), dim3(256), 0, s, a);          \
+  } while (0)
   if (dtype == 0) {
     if (mode == 0) LLK_NORM(float, 0);
     else if (mode == 1) LLK_NORM(float, 1);

@@ -134,10 +134,11 @@ def test_prefill_c2_bf16():
     assert_argmax(nid.cpu().numpy(), ref["logits"], "c2 argmax")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_decode_ragged_positions_match_oracle(dtype):
+@pytest.mark.parametrize("dtype,D,H,G", [("bf16", 512, 8, 2), ("f32", 512, 8, 2), ("bf16", 1024, 8, 2),
+                                         ("bf16", 1024, 8, 1), ("bf16", 768, 8, 2)])
+def test_decode_ragged_positions_match_oracle(dtype, D, H, G):
     # prefill S tokens into the cache, then one decode step with per-sequence positions
-    cfg = small_cfg(dtype, 512, 8, 2, 40, 3, L=2, V=3000, seed=21).with_(kind="prefill")
+    cfg = small_cfg(dtype, D, H, G, 40, 3, L=2, V=3000, seed=21).with_(kind="prefill")
     say(f"case decode ragged {cfg.key}")
     S, B = cfg.seq_len, cfg.batch
     cap = 64
@@ -221,3 +222,38 @@ def test_c3_layer_s2048_sampled_rows():
     rows = [0, 1, 63, 64, 255, 1000, 1537, 2047]
     ref = OR.layer(cfg, x, rows=rows)["y"]
     assert_close(host(y)[:, rows], ref, BF16_TOL, "c3 s2048 sampled rows")
+
+
+def test_decode_8b_shapes_two_layers_sampled_sequences():
+    # batch 64 over seeded caches of 4096 positions at 8B shapes; two layers; sequences sampled for the oracle
+    cfg = I.CONFIGS["c5"].with_(n_layers=2)
+    say("case decode 8B shapes, 2 layers, B=64, cache 4096")
+    dm = R.DeviceModel(cfg)
+    B, P, cap = cfg.batch, cfg.cache_len, cfg.cache_cap
+    caches = []
+    for l in range(cfg.n_layers):
+        pair = []
+        for which in ("k", "v"):
+            t = torch.zeros((B, cap, cfg.n_kv_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+            t[:, :P] = R.bits_to_device(I.kv_cache_bits(cfg, l, which))
+            pair.append(t)
+        caches.append(tuple(pair))
+    ids = I.prompt_ids(cfg).reshape(-1).astype(np.int32)
+    pos = torch.full((B,), P, dtype=torch.int32, device="cuda")
+    logits = torch.empty((B, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    nid = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = R.workspace(dm.args, B, 1)
+    M.llama_decode_step(dm.args, dm.struct, torch.from_numpy(ids).cuda(), pos, B, M.kv_array(caches),
+                        logits=logits, next_id=nid, ws=ws)
+    torch.cuda.synchronize()
+    seqs = [0, 29, 63]
+    new_kv = []
+    ref = OR.decode(cfg, seqs, new_kv=new_kv)
+    got = host(logits)[seqs]
+    assert_close(got, ref["logits"], BF16_TOL, "decode logits (sampled sequences)")
+    assert float(np.max(np.abs(got - ref["logits"]))) < 1e-3 * float(np.max(np.abs(ref["logits"])))
+    assert_argmax(nid.cpu().numpy()[seqs], ref["logits"], "decode argmax (sampled sequences)")
+    for (bi, l, kn, vn) in new_kv:
+        b = seqs[bi]
+        assert_close(host(caches[l][0][b, P]), kn, BF16_TOL, f"new k seq {b} layer {l}")
+        assert_close(host(caches[l][1][b, P]), vn, BF16_TOL, f"new v seq {b} layer {l}")
