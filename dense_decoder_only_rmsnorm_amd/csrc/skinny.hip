@@ -7,11 +7,17 @@
 // carrying ~16 significant bits; both planes are multiplied against the same
 // weight fragment (two MFMAs), so the weight bytes do not change.
 //
-// A block of 256 threads owns 64 B-rows (four 16-column MFMA blocks) and one
-// K slice (grid.y); its four waves take interleaved 32-wide K steps and are
-// summed through LDS at the end.  MFMA 16x16x32 (v_mfma_f32_16x16x32_bf16):
-// lane l supplies row/column (l % 16) and eight consecutive k at 8*(l / 16);
-// output register r of lane l holds row 4*(l/16) + r, column l % 16.
+// A block of 256 threads owns 64 B-rows (four 16-column MFMA blocks, one per
+// wave) and one K slice (grid.y).  The K slice streams through three LDS
+// stages of 64 k: weights and both activation planes arrive with
+// global_load_lds_dwordx4 in fully coalesced 1 KB pieces (8 rows x 128
+// bytes), stored with the 16-byte chunk swizzle c ^ ((row >> 1) & 7) so the
+// MFMA fragment reads of 16 consecutive rows are bank-conflict free.  Loading
+// fragments straight from global memory in MFMA layout would make every
+// quarter-wave touch 16 different rows.  The activations are shared by the
+// four waves through LDS.  MFMA 16x16x32 (v_mfma_f32_16x16x32_bf16): lane l
+// supplies row/column (l % 16) and eight consecutive k at 8*(l / 16); output
+// register r of lane l holds row 4*(l/16) + r, column l % 16.
 //
 // Epilogues:
 //   SK_PARTIAL       fp32 split-K partial [ks][M][N] (summed by the consumer)
@@ -27,109 +33,137 @@ namespace llk {
 
 namespace {
 
+constexpr int SK_KCH = 64;     // k per LDS stage
+constexpr int SK_STAGES = 3;
+constexpr int SK_ROWB = SK_KCH * 2;  // bytes per tile row (128)
+
 template <int MB, int EPI>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
-  extern __shared__ __align__(16) float red[];  // [4 waves][MB][4][4][64]
+  // stage layout (bf16): A hi [64][64], A lo [64][64], B [64][64]
+  constexpr int ST_ELEMS = 3 * 64 * SK_KCH;
+  extern __shared__ __align__(16) u16 sm[];  // [SK_STAGES][ST_ELEMS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk0 = blockIdx.x;
   const int ks = blockIdx.y;
   const int Kc = a.K / a.ksplit;
   const int kbeg = ks * Kc;
-  const int l16 = lane & 15, lk = (lane >> 4) * 8;
+  const int nchunk = Kc / SK_KCH;
 
-  // weight rows of this lane for each of the four 16-column blocks
-  const u16 *brow[4];
-  bool bok[4];
+  // Loader: 24 pieces of 1 KB per stage (A hi 8, A lo 8, B 8); wave w issues
+  // pieces w, w+4, ...  Piece p covers tile rows 8*(p%8) .. +7 of its matrix;
+  // lane L -> row 8*(p%8) + L/8, physical chunk L%8 holding logical chunk
+  // (L%8) ^ ((row >> 1) & 7).  Rows past M or past the weight read a clamped
+  // valid row: they only feed outputs that are never stored.
+  const int lr = lane >> 3, lq = lane & 7;
+  const u16 *src[6];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    int wr;
+  for (int i = 0; i < 6; ++i) {
+    const int p = wave + 4 * i;        // 0..23
+    const int mat = p >> 3;            // 0: A hi, 1: A lo, 2: B
+    const int row = (p & 7) * 8 + lr;  // tile row 0..63
+    const int c = lq ^ ((row >> 1) & 7);
     const u16 *base;
-    bool ok;
-    if (EPI == SK_SWIGLU_HILO || EPI == SK_SWIGLU_BF16) {
-      const int F = a.N / 2;
-      wr = nblk0 * 32 + (nb & 1) * 16 + l16;
-      base = nb < 2 ? a.B0 : a.B1;
-      ok = wr < F;
+    int64_t ld;
+    int grow;
+    if (mat < 2) {
+      grow = min(row, a.M - 1);
+      base = a.A + (mat == 1 && a.use_lo ? a.a_plane : 0);
+      ld = a.lda;
     } else {
-      const int n = nblk0 * 64 + nb * 16 + l16;
-      ok = n < a.N;
-      if (a.nq > 0) {
-        base = n < a.nq ? a.B0 : (n < a.nq + a.nk ? a.B1 : a.B2);
-        wr = n < a.nq ? n : (n < a.nq + a.nk ? n - a.nq : n - a.nq - a.nk);
+      int wr;
+      if (EPI == SK_SWIGLU_HILO || EPI == SK_SWIGLU_BF16) {
+        // tile rows: [gate 0-15 | up 0-15 | gate 16-31 | up 16-31] of this block's 32 output columns
+        const int F = a.N / 2;
+        wr = min(nblk0 * 32 + (row >> 5) * 16 + (row & 15), F - 1);
+        base = ((row >> 4) & 1) ? a.B1 : a.B0;
       } else {
-        base = a.B0;
-        wr = n;
+        const int n = min(nblk0 * 64 + row, a.N - 1);
+        if (a.nq > 0) {
+          base = n < a.nq ? a.B0 : (n < a.nq + a.nk ? a.B1 : a.B2);
+          wr = n < a.nq ? n : (n < a.nq + a.nk ? n - a.nq : n - a.nq - a.nk);
+        } else {
+          base = a.B0;
+          wr = n;
+        }
+      }
+      grow = wr;
+      ld = a.K;
+    }
+    src[i] = base + (int64_t)grow * ld + kbeg + c * 8;
+  }
+  auto issue = [&](int stage, int chunk) {
+    u16 *st = sm + stage * ST_ELEMS;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int p = __builtin_amdgcn_readfirstlane(wave + 4 * i);
+      u16 *dst = st + (p >> 3) * 64 * SK_KCH + (p & 7) * 8 * SK_KCH;
+      __builtin_amdgcn_global_load_lds((const void *)(src[i] + chunk * SK_KCH),
+                                       (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
+  };
+
+  // fragment offsets: row (lane % 16) of a 16-row block, logical chunk 4*kk + lane/16
+  const int frow = lane & 15;
+  const int sw = (frow >> 1) & 7;
+  f32x4 acc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  if (nchunk > 1) issue(1, 1);
+  for (int ch = 0; ch < nchunk; ++ch) {
+    // wait for this wave's pieces of stage ch (the later stage may stay in flight)
+    if (ch + 1 < nchunk)
+      __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): one later stage of 6 loads outstanding
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // every wave's pieces of this stage are in LDS, and every wave is done
+    // reading the stage that the next issue overwrites.  (A plain
+    // __syncthreads would also wait for the stage still in flight.)
+    asm volatile("s_barrier" ::: "memory");
+    if (ch + 2 < nchunk) issue((ch + 2) % SK_STAGES, ch + 2);
+    const u16 *st = sm + (ch % SK_STAGES) * ST_ELEMS;
+    const u16 *bp = st + 2 * 64 * SK_KCH + (wave * 16 + frow) * SK_KCH;
+#pragma unroll
+    for (int kk = 0; kk < SK_KCH / 32; ++kk) {
+      const int co = ((4 * kk + (lane >> 4)) ^ sw) * 8;
+      const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(bp + co);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const u16 *ap = st + (mb * 16 + frow) * SK_KCH + co;
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(ap), bb, acc[mb], 0, 0, 0);
+        if (a.use_lo)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(ap + 64 * SK_KCH), bb,
+                                                            acc[mb], 0, 0, 0);
       }
     }
-    bok[nb] = ok;
-    brow[nb] = base + (int64_t)(ok ? wr : 0) * a.K + kbeg + lk;
   }
-  const u16 *arow[MB];
-  bool aok[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int r = mb * 16 + l16;
-    aok[mb] = r < a.M;
-    arow[mb] = a.A + (int64_t)(aok[mb] ? r : 0) * a.lda + kbeg + lk;
-  }
+  __syncthreads();  // stages are reused for the epilogue
 
-  f32x4 acc[MB][4];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nsteps = Kc / 32;
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  for (int st = wave; st < nsteps; st += 4) {
-    const int k = st * 32;
-    uint4 bv[4], ah[MB], al[MB];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) bv[nb] = bok[nb] ? *reinterpret_cast<const uint4 *>(brow[nb] + k) : z;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      ah[mb] = aok[mb] ? *reinterpret_cast<const uint4 *>(arow[mb] + k) : z;
-      al[mb] = (aok[mb] && a.use_lo) ? *reinterpret_cast<const uint4 *>(arow[mb] + a.a_plane + k) : z;
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<bf16x8 *>(&ah[mb]),
-                                                              *reinterpret_cast<bf16x8 *>(&bv[nb]), acc[mb][nb], 0, 0, 0);
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<bf16x8 *>(&al[mb]),
-                                                              *reinterpret_cast<bf16x8 *>(&bv[nb]), acc[mb][nb], 0, 0, 0);
-      }
-    }
-  }
-
-  // cross-wave reduction through LDS: red[w][mb][nb][r][lane]
+  // wave w holds column block w: acc[mb][r] = C[mb*16 + 4*(lane/16) + r][16w + lane%16]
+  float *red = reinterpret_cast<float *>(sm);  // [MB*16 rows][64 cols]
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[(((wave * MB + mb) * 4 + nb) * 4 + r) * 64 + lane] = acc[mb][nb][r];
+    for (int r = 0; r < 4; ++r) red[(mb * 16 + 4 * (lane >> 4) + r) * 64 + wave * 16 + frow] = acc[mb][r];
   __syncthreads();
-  constexpr int PER_W = MB * 4 * 4 * 64;
-  auto total = [&](int e) { return red[e] + red[PER_W + e] + red[2 * PER_W + e] + red[3 * PER_W + e]; };
+  constexpr int ROWS = MB * 16;
 
   if (EPI == SK_PARTIAL) {
     float *C = static_cast<float *>(a.C) + (int64_t)ks * a.c_plane;
-    for (int e = tid; e < PER_W; e += 256) {
-      const int ln = e & 63, r = (e >> 6) & 3, nb = (e >> 8) & 3, mb = e >> 10;
-      const int row = mb * 16 + 4 * (ln >> 4) + r, col = nblk0 * 64 + nb * 16 + (ln & 15);
-      if (row < a.M && col < a.N) C[(int64_t)row * a.N + col] = total(e);
+    for (int e = tid; e < ROWS * 64; e += 256) {
+      const int row = e >> 6, col = nblk0 * 64 + (e & 63);
+      if (row < a.M && col < a.N) C[(int64_t)row * a.N + col] = red[e];
     }
   } else if (EPI == SK_SWIGLU_HILO || EPI == SK_SWIGLU_BF16) {
     const int F = a.N / 2;
     u16 *C = static_cast<u16 *>(a.C);
-    for (int e = tid; e < PER_W; e += 256) {
-      const int ln = e & 63, r = (e >> 6) & 3, nb = (e >> 8) & 3, mb = e >> 10;
-      if (nb >= 2) continue;
-      const int row = mb * 16 + 4 * (ln >> 4) + r, col = nblk0 * 32 + nb * 16 + (ln & 15);
+    for (int e = tid; e < ROWS * 32; e += 256) {
+      const int row = e >> 5, uc = e & 31;
+      const int gc = (uc >> 4) * 32 + (uc & 15);  // gate column in the tile; up is 16 further
+      const int col = nblk0 * 32 + uc;
       if (row < a.M && col < F) {
-        const float g = total(e), up = total(e + 2 * 256);
+        const float g = red[row * 64 + gc], up = red[row * 64 + gc + 16];
         const float u = silu(g) * up;
         const int64_t o = (int64_t)row * F + col;
         if (EPI == SK_SWIGLU_HILO) {
@@ -143,27 +177,20 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
       }
     }
   } else {  // SK_LOGITS
-    __syncthreads();
-    // fold the four waves into red[0 .. PER_W) first
-    for (int e = tid; e < PER_W; e += 256) red[e] = total(e);
-    __syncthreads();
     if (a.logits) {
-      for (int e = tid; e < PER_W; e += 256) {
-        const int ln = e & 63, r = (e >> 6) & 3, nb = (e >> 8) & 3, mb = e >> 10;
-        const int row = mb * 16 + 4 * (ln >> 4) + r, col = nblk0 * 64 + nb * 16 + (ln & 15);
+      for (int e = tid; e < ROWS * 64; e += 256) {
+        const int row = e >> 6, col = nblk0 * 64 + (e & 63);
         if (row < a.M && col < a.N) a.logits[(int64_t)row * a.N + col] = red[e];
       }
     }
-    if (tid < MB * 16) {
+    if (tid < ROWS) {
       const int row = tid;
-      const int mb = row >> 4, q = (row & 15) >> 2, r = row & 3;
       float bv = -INFINITY;
       int bi = 0x7fffffff;
       for (int c = 0; c < 64; ++c) {
-        const int nb = c >> 4, cl = c & 15;
         const int col = nblk0 * 64 + c;
         if (col >= a.N) break;
-        const float v = red[((mb * 4 + nb) * 4 + r) * 64 + q * 16 + cl];
+        const float v = red[row * 64 + c];
         if (v > bv) { bv = v; bi = col; }  // ascending columns: first maximum kept
       }
       if (row < a.M) {
@@ -174,19 +201,27 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
   }
 }
 
+template <int MB, int EPI>
+hipError_t launch_one(const SkinnyArgs &a, dim3 grid, size_t lds, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny_kernel<MB, EPI>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  (void)attr;
+  hipLaunchKernelGGL((skinny_kernel<MB, EPI>), grid, dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
 template <int MB>
 hipError_t launch_mb(int epi, const SkinnyArgs &a, hipStream_t s) {
   const int nblk = (epi == SK_SWIGLU_HILO || epi == SK_SWIGLU_BF16) ? (a.N / 2 + 31) / 32 : (a.N + 63) / 64;
   dim3 grid(nblk, a.ksplit);
-  const size_t lds = (size_t)4 * MB * 4 * 4 * 64 * sizeof(float);
+  const size_t lds = (size_t)SK_STAGES * 3 * 64 * SK_KCH * sizeof(u16);  // >= the epilogue's 64 x 64 floats
   switch (epi) {
-    case SK_PARTIAL: hipLaunchKernelGGL((skinny_kernel<MB, SK_PARTIAL>), grid, dim3(256), lds, s, a); break;
-    case SK_SWIGLU_HILO: hipLaunchKernelGGL((skinny_kernel<MB, SK_SWIGLU_HILO>), grid, dim3(256), lds, s, a); break;
-    case SK_SWIGLU_BF16: hipLaunchKernelGGL((skinny_kernel<MB, SK_SWIGLU_BF16>), grid, dim3(256), lds, s, a); break;
-    case SK_LOGITS: hipLaunchKernelGGL((skinny_kernel<MB, SK_LOGITS>), grid, dim3(256), lds, s, a); break;
-    default: return hipErrorInvalidValue;
+    case SK_PARTIAL: return launch_one<MB, SK_PARTIAL>(a, grid, lds, s);
+    case SK_SWIGLU_HILO: return launch_one<MB, SK_SWIGLU_HILO>(a, grid, lds, s);
+    case SK_SWIGLU_BF16: return launch_one<MB, SK_SWIGLU_BF16>(a, grid, lds, s);
+    case SK_LOGITS: return launch_one<MB, SK_LOGITS>(a, grid, lds, s);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 }  // namespace
 
