@@ -244,6 +244,7 @@ struct DecodeWs {
   float *qkv_part;  // bf16: [ks1][B][Nqkv]; fp32: [B][Nqkv]
   float *q;         // [B][Hq]
   u16 *qhl;         // bf16 path: [2][B][Hq] (q scaled into log2 units)
+  float *knew, *vnew;  // [B][G*hd] fp32: the new token's rotated key and value
   float *pm, *pl, *po;
   void *o;          // bf16 hi/lo [2][B][Hq] or fp32 [B][Hq]
   float *wo_part;   // [ks2][B][D]
@@ -264,6 +265,8 @@ DecodeWs carve_decode(Carver &c, const Dims &d, int B, int cap) {
   w.tab = c.take<float2>(Bz * (d.hd / 2));
   w.q = c.take<float>(Bz * d.Hq());
   w.qhl = c.take<u16>(2 * Bz * d.Hq());
+  w.knew = c.take<float>(Bz * d.Hk());
+  w.vnew = c.take<float>(Bz * d.Hk());
   w.pm = c.take<float>(Bz * d.H * w.nchunk);
   w.pl = c.take<float>(Bz * d.H * w.nchunk);
   w.po = c.take<float>(Bz * d.H * w.nchunk * d.hd);
@@ -680,14 +683,20 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
     ra.qscale = (float)(1.4426950408889634 / sqrt((double)d.hd));
     ra.kc = kv[l].k;
     ra.vc = kv[l].v;
+    ra.knew = dw.knew;
+    ra.vnew = dw.vnew;
     LAUNCH("rope_qkv", launch_rope_qkv(d.dt, ra, s));
-    // a7: attention over the cache
+    // a7: attention over the cache; the token's own key and value enter
+    // unrounded (fp32) through the combine step, the cache keeps them in the
+    // storage type for later steps
     DecodeAttnArgs da{};
     da.q = dw.q;
     da.qhl = bf ? dw.qhl : nullptr;
     da.k = kv[l].k;
     da.v = kv[l].v;
     da.pos = pos;
+    da.knew = dw.knew;
+    da.vnew = dw.vnew;
     da.cap = cap;
     da.B = B;
     da.H = d.H;

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecodeAttnArgs a) {
   int pb = a.pos[b];
   pb = pb < 0 ? 0 : (pb > a.cap - 1 ? a.cap - 1 : pb);
   const int c0 = ci * CH;
-  const int kend = min(c0 + CH, pb + 1);
+  const int kend = min(c0 + CH, a.knew ? pb : pb + 1);  // own position added by the combine when knew is set
   const int64_t pidx = ((int64_t)b * a.H + g * n_rep) * a.nchunk + ci;  // + r * nchunk per head
   if (c0 >= kend) {
     for (int i = tid; i < n_rep * HD; i += 256) {
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(DecodeAttnArgs a) {
   int pb = a.pos[b];
   pb = pb < 0 ? 0 : (pb > a.cap - 1 ? a.cap - 1 : pb);
   const int c0 = ci * CH;
-  const int kend = min(c0 + CH, pb + 1);
+  const int kend = min(c0 + CH, a.knew ? pb : pb + 1);  // own position added by the combine when knew is set
   const int64_t pidx = ((int64_t)b * a.H + g * n_rep) * a.nchunk + ci;
   if (c0 >= kend) {
     for (int i = tid; i < n_rep * HD; i += 256) a.po[(pidx + (int64_t)(i / HD) * a.nchunk) * HD + i % HD] = 0.f;
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma2(DecodeAttnArgs a) {
   int pb = a.pos[b];
   pb = pb < 0 ? 0 : (pb > a.cap - 1 ? a.cap - 1 : pb);
   const int c0 = ci * CH;
-  const int kend = min(c0 + CH, pb + 1);
+  const int kend = min(c0 + CH, a.knew ? pb : pb + 1);  // own position added by the combine when knew is set
   const int64_t pidx = ((int64_t)b * a.H + g * n_rep) * a.nchunk + ci;
   if (c0 >= kend) {
     for (int i = tid; i < n_rep * HD; i += 256) a.po[(pidx + (int64_t)(i / HD) * a.nchunk) * HD + i % HD] = 0.f;
@@ -680,13 +680,38 @@ __global__ __launch_bounds__(256) void attn_decode_mfma2(DecodeAttnArgs a) {
 
 // Combine the chunk partials of one (sequence, head); maxima are in log2
 // units: O = sum_c 2^{m_c - M} o_c / sum_c 2^{m_c - M} l_c, M = max_c m_c.
+// With knew/vnew the query's own key and value join as one more partial
+// (m = q.k_new * scale * log2 e, l = 1, o = v_new), all in fp32.
 template <int HD>
-__global__ __launch_bounds__(HD) void attn_combine_kernel(DecodeAttnArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(((HD + 63) / 64) * 64) void attn_combine_kernel(DecodeAttnArgs a) {
+  constexpr int NW = (HD + 63) / 64;  // whole waves; lanes d >= HD only join the reduction
+  __shared__ float red[NW];
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const bool on = t < HD;
+  const int d = on ? t : HD - 1;
   const int64_t base = ((int64_t)b * a.H + h) * a.nchunk;
-  float M = -INFINITY;
+  float ms = -INFINITY, vself = 0.f;
+  if (a.knew) {
+    const int g = h / (a.H / a.G);
+    const int64_t kv = ((int64_t)b * a.G + g) * HD + d;
+    float qk = on ? a.q[((int64_t)b * a.H + h) * HD + d] * a.knew[kv] : 0.f;
+    qk = wave_sum(qk);
+    if ((t & 63) == 0) red[t >> 6] = qk;
+    __syncthreads();
+    float dot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) dot += red[w];
+    ms = dot * a.scale * kLog2e;
+    vself = a.vnew[kv];
+  }
+  float M = ms;
   for (int c = 0; c < a.nchunk; ++c) M = fmaxf(M, a.pm[base + c]);
   float L = 0.f, acc = 0.f;
+  if (a.knew) {
+    const float w = exp2f(ms - M);
+    L = w;
+    acc = w * vself;
+  }
   for (int c = 0; c < a.nchunk; ++c) {
     const float mc = a.pm[base + c];
     if (mc == -INFINITY) continue;
@@ -694,6 +719,7 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(DecodeAttnArgs a) {
     L += w * a.pl[base + c];
     acc += w * a.po[(base + c) * HD + d];
   }
+  if (!on) return;
   const float v = acc / L;
   const int64_t o = (int64_t)b * a.H * HD + h * HD + d;
   if (a.out_mode == 0) {
@@ -751,7 +777,7 @@ hipError_t launch_attn_prefill(int dtype, const AttnArgs &a, hipStream_t s) {
 hipError_t launch_attn_combine(const DecodeAttnArgs &a, hipStream_t s) {
   switch (a.hd) {
     case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(a.H, a.B), dim3(64), 0, s, a); break;
-    case 96: hipLaunchKernelGGL(attn_combine_kernel<96>, dim3(a.H, a.B), dim3(96), 0, s, a); break;
+    case 96: hipLaunchKernelGGL(attn_combine_kernel<96>, dim3(a.H, a.B), dim3(128), 0, s, a); break;
     case 128: hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(a.H, a.B), dim3(128), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }

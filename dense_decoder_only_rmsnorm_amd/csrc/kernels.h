@@ -34,6 +34,7 @@ struct RopeQkvArgs {
   uint16_t *qhl;       // optional: q * qscale as bf16 hi/lo planes [2][rows][H*hd]
   float qscale;
   void *kc, *vc;       // [B][cap][G][hd] (dtype)
+  float *knew, *vnew;  // optional: rotated k and v of each row in fp32, [rows][G*hd]
 };
 
 // Dense bf16 GEMM C = A * B^T on MFMA with fused epilogues (prefill).
@@ -88,6 +89,10 @@ struct DecodeAttnArgs {
   const uint16_t *qhl;                    // q * scale * log2(e) as bf16 hi/lo planes [2][B][H*hd] (bf16 path)
   const void *k; const void *v;           // [B][cap][G][hd] (dtype)
   const int32_t *pos;                     // [B] query positions (inclusive key range 0..pos)
+  // optional [B][G][hd] fp32 key/value of the query's own position: when set,
+  // the chunk kernels cover cached keys 0..pos-1 and the combine kernel adds
+  // the query's own term from these unrounded values
+  const float *knew; const float *vnew;
   int cap, B, H, G, hd, chunk, nchunk;
   float scale;
   float *pm; float *pl; float *po;        // partials [B][H][nchunk] (m, l), [B][H][nchunk][hd]

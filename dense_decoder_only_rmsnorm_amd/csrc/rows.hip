@@ -197,6 +197,8 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(RopeQkvArgs a) {
     TC *dst = base + (((int64_t)b * a.cap + p) * a.G + g) * a.hd + d;
     Elem<TC>::store(dst, x0);
     Elem<TC>::store(dst + 1, x1);
+    float *fn = isk ? a.knew : a.vnew;
+    if (fn) *reinterpret_cast<float2 *>(fn + (int64_t)r * Hk + c) = make_float2(x0, x1);
   }
 }
 

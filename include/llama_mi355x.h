@@ -145,7 +145,8 @@ int llama_prefill(const llama_args *a, const llama_model_w *w, const int32_t *id
  *       new key/value go to cache slot pos[b] and the token attends to
  *       positions 0..pos[b] [P2 3.4 inference branch].  Each pos[b] must lie
  *       in [0, max_seq_len); out-of-range entries are clamped by the kernels
- *       so no access leaves the cache.
+ *       so no access leaves the cache.  The cache stores the new key/value
+ *       in `dtype`; the token's own attention uses them unrounded (fp32).
  *   kv  HOST array of n_layers llama_kv (required)
  *   logits nullable [batch][vocab] fp32; next_id [batch] int32 (device).
  * Errors: ERR_ARG (null ids/pos/kv/next_id), ERR_SHAPE (batch >
