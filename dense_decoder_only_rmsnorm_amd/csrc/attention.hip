@@ -15,6 +15,8 @@
 //                 per thread).
 // attn_decode     one query per sequence over the KV cache, split into key
 //                 chunks (partial max / sum / output), then combined.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -191,9 +193,9 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(AttnArgs a) {
 //   O^T += V^T P^T   A = V^T read from row-major V with ds_read_b64_tr_b16,
 //                    B = P^T taken from the score registers as bf16.
 // K and V arrive with global_load_lds_dwordx4 (no VGPR round trip) while the
-// previous tile is being computed; 256-byte rows keep each 16-byte chunk c of
-// key row r at c ^ (r & 15), so the 32 rows a fragment read touches fall in
-// distinct banks.
+// previous tile is being computed.  Rows are 256 bytes; K and Q keep 16-byte
+// chunk c of row r at c ^ (r & 15), so the 32 rows a fragment read touches
+// fall in distinct banks; V uses the swizzle its transposed reads need.
 // Block order: consecutive block ids cycle through the KV groups, so the
 // blocks one XCD receives (ids congruent mod 8) share a group's K/V in L2;
 // within a group the longest causal ranges start first.
@@ -259,12 +261,17 @@ __global__ __launch_bounds__(256) void attn_fwd_tiled128(AttnArgs a) {
 
   // loader: piece p = wave + 4i (i < 4) covers tile rows 4p .. 4p+3; lane L
   // -> row 4p + L/16, physical chunk L%16 holding logical chunk (L%16)^(row&15)
-  int lrow[4], lcol[4];
+  // V rows use a second swizzle, vswz(r) = ((r & 3) << 2) | ((r >> 2) & 3):
+  // a transposed read touches 4 consecutive rows x 4 chunks, and this spreads
+  // them over all 16 chunk positions (r & 15 would keep them in one group of
+  // four and serialise the read 4 ways).
+  int lrow[4], lcol[4], lcolv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = wave + 4 * i;
     lrow[i] = 4 * p + (lane >> 4);
     lcol[i] = ((lane & 15) ^ (lrow[i] & 15)) * 8;
+    lcolv[i] = ((lane & 15) ^ (((lrow[i] & 3) << 2) | ((lrow[i] >> 2) & 3))) * 8;
   }
   auto issue = [&](int kt, int buf) {
     const int k0 = kt * KT;
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(256) void attn_fwd_tiled128(AttnArgs a) {
       const int p = __builtin_amdgcn_readfirstlane(wave + 4 * i);
       __builtin_amdgcn_global_load_lds((const void *)(Kg + (int64_t)key * kstride + lcol[i]),
                                        (__attribute__((address_space(3))) void *)(Ks[buf] + p * 4 * HD), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(Vg + (int64_t)key * kstride + lcol[i]),
+      __builtin_amdgcn_global_load_lds((const void *)(Vg + (int64_t)key * kstride + lcolv[i]),
                                        (__attribute__((address_space(3))) void *)(Vs[buf] + p * 4 * HD), 16, 0, 0);
     }
   };
@@ -296,12 +303,11 @@ __global__ __launch_bounds__(256) void attn_fwd_tiled128(AttnArgs a) {
   const int vr0 = 4 * hf + (jj >> 2);
   const int vq = 2 * dg + ((jj & 3) >> 1), vhalf = (jj & 1) * 4;
 
-  issue(0, 0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();  // tile kt has landed; every wave is done with tile kt-1
-    if (kt + 1 < ntiles) issue(kt + 1, (kt + 1) & 1);
+  // one 64-key tile: MASK is true only for tiles that reach past the
+  // wave's smallest query position
+  auto tile = [&](int kt, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
     const int k0 = kt * KT;
-    if (k0 > wmax) continue;  // every key of this tile lies past this wave's queries
     const u16 *ks = Ks[kt & 1];
     const u16 *vs = Vs[kt & 1];
 
@@ -326,10 +332,9 @@ __global__ __launch_bounds__(256) void attn_fwd_tiled128(AttnArgs a) {
       }
     }
     // online softmax per query, in log2 units.  The running maximum m only
-    // moves when a tile's maximum exceeds it by more than 8 (then P stays
+    // moves when a tile's maximum exceeds it by more than 8 (P then stays
     // below 2^8 and the sum l uses the same m, so the result is exact); the
     // rescale of O is therefore rare and wave-uniform.
-    const bool need_mask = k0 + KT - 1 > wmin;
     float tmax[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -338,13 +343,11 @@ __global__ __launch_bounds__(256) void attn_fwd_tiled128(AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float v = sc[kb][qb][r];
-          if (need_mask) {
+          if (MASK) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            v = key <= qpos[qb] ? v : -INFINITY;
-            sc[kb][qb][r] = v;
+            if (key > qpos[qb]) sc[kb][qb][r] = -INFINITY;
           }
-          mx = fmaxf(mx, v);
+          mx = fmaxf(mx, sc[kb][qb][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
       tmax[qb] = mx * c;  // c > 0: the maximum commutes with the scale
@@ -354,7 +357,7 @@ __global__ __launch_bounds__(256) void attn_fwd_tiled128(AttnArgs a) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const float m_new = fmaxf(m[qb], tmax[qb]);  // finite: key 0 is visible to every query
-        const float alpha = exp2f(m[qb] - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_new);
         l[qb] *= alpha;
         m[qb] = m_new;
 #pragma unroll
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(256) void attn_fwd_tiled128(AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(fmaf(sc[kb][qb][r], c, -m[qb]));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][r], c, -m[qb]));
           sc[kb][qb][r] = p;
           rs += p;
         }
@@ -395,7 +398,8 @@ __global__ __launch_bounds__(256) void attn_fwd_tiled128(AttnArgs a) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int r = rbase + 8 * h2;
-          const int off = (r * HD + (((4 * ob + vq) ^ (r & 15)) * 8) + vhalf) * (int)sizeof(u16);
+          const int vsw = ((r & 3) << 2) | ((r >> 2) & 3);
+          const int off = (r * HD + (((4 * ob + vq) ^ vsw) * 8) + vhalf) * (int)sizeof(u16);
           const v4s w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) v4s *)((__attribute__((address_space(3))) const char *)vs + off));
           wv[h2] = __builtin_bit_cast(u32x2, w);
@@ -406,6 +410,20 @@ __global__ __launch_bounds__(256) void attn_fwd_tiled128(AttnArgs a) {
           o[qb][ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], o[qb][ob], 0, 0, 0);
       }
     }
+  };
+
+  // tiles [0, nfull) are visible to every query of this wave; the rest are
+  // masked, and tiles past the wave's last query are skipped.  Every wave
+  // passes the same ntiles barriers.
+  const int nfull = min(ntiles, (wmin + 1) / KT);
+  issue(0, 0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    __syncthreads();  // tile kt has landed; every wave is done with tile kt-1
+    if (kt + 1 < ntiles) issue(kt + 1, (kt + 1) & 1);
+    if (kt < nfull)
+      tile(kt, std::integral_constant<bool, false>());
+    else if (kt * KT <= wmax)
+      tile(kt, std::integral_constant<bool, true>());
   }
 
   // lane holds O^T[d = 32*ob + 8*(r/4) + 4*hf + r%4][query lane%32]
