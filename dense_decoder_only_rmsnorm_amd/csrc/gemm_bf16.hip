@@ -139,11 +139,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
         for (int j = 0; j < FN; ++j)
           bfr[cb ^ 1][j] = *reinterpret_cast<const bf16x8 *>(Bb + j * 32 * RS + koff[kk + 1]);
       }
+      // keep the next step's fragment reads ahead of this step's MFMAs (the
+      // scheduler would otherwise sink each read next to its use and expose
+      // the LDS latency once per MFMA group)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();  // the next stage has landed (waits for this wave's loads) and this one is free
   }
@@ -152,25 +157,36 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const int col_l = lane & 31;
   const int rloc = wm * WM + 4 * (lane >> 5);  // tile-local row base of this lane
   if (EPI == EPI_RESID || EPI == EPI_STORE_F32) {
-    // fp32 outputs: each store instruction writes 32 consecutive floats of a row
+    // fp32 outputs: each store instruction writes 32 consecutive floats of a
+    // row.  The residual loads of one 32-row block (FN x 16 per lane) are
+    // issued together from clamped, always valid addresses, so they overlap
+    // instead of each waiting for the previous one; only stores are guarded.
+    float *C = static_cast<float *>(a.C);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      float rv[FN][16];
+      if (EPI == EPI_RESID) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = min(n0 + wn * WN + j * 32 + col_l, a.N - 1);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = min(m0 + rloc + i * 32 + 8 * (r / 4) + (r % 4), a.M - 1);
+            rv[j][r] = a.R[(int64_t)row * a.ldr + col];
+          }
+        }
+      }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int col = n0 + wn * WN + j * 32 + col_l;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + rloc + i * 32 + 8 * (r / 4) + (r % 4);
-          if (row < a.M && col < a.N) {
-            const float v = acc[i][j][r];
-            float *C = static_cast<float *>(a.C);
-            if (EPI == EPI_RESID)
-              C[(int64_t)row * a.ldc + col] = a.R[(int64_t)row * a.ldr + col] + v;
-            else
-              C[(int64_t)row * a.ldc + col] = v;
-          }
+          const float v = EPI == EPI_RESID ? rv[j][r] + acc[i][j][r] : acc[i][j][r];
+          if (row < a.M && col < a.N) C[(int64_t)row * a.ldc + col] = v;
         }
       }
+    }
     return;
   }
 
@@ -179,6 +195,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int CN = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
   constexpr int LDC = CN + 8;
   u16 *Cs = smem;  // [BM][LDC], reuses the operand buffers (loop ended with a barrier)
+  // sequence positions (row % S) of this lane's rows, for the RoPE table:
+  // one division per thread, then wrap-around steps
+  int tpos[EPI == EPI_QKV_ROPE ? FM : 1][16];
+  if (EPI == EPI_QKV_ROPE) {
+    const int pbase = m0 % a.S;  // position of tile row 0
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // tile row of this value, clamped to the last row of the matrix (>= 0: the tile starts inside it)
+        const int x = min(rloc + i * 32 + 8 * (r / 4) + (r % 4), a.M - 1 - m0);
+        int p = pbase + x;
+        while (p >= a.S) p -= a.S;
+        tpos[i][r] = p;
+      }
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -199,16 +231,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
           const bool rot = col < Hq + Hk;
           const int d = (col < Hq ? col : col - Hq) % a.hd;
           const bool odd = col & 1;
+          // the 16 table entries of this block are loaded together (valid
+          // addresses for every lane), then applied
+          float2 cs[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cs[r] = a.tab[(int64_t)tpos[i][r] * (a.hd / 2) + d / 2];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rr = rloc + i * 32 + 8 * (r / 4) + (r % 4);
             float v = acc[i][j][r];
             const float pv = __shfl_xor(v, 1, kWave);
-            if (rot) {
-              const int row = min(m0 + rr, a.M - 1);
-              const float2 cs = a.tab[(int64_t)(row % a.S) * (a.hd / 2) + d / 2];
-              v = odd ? pv * cs.y + v * cs.x : v * cs.x - pv * cs.y;
-            }
+            if (rot) v = odd ? pv * cs[r].y + v * cs[r].x : v * cs[r].x - pv * cs[r].y;
             Cs[rr * LDC + ccol] = f2bf(v);
           }
         } else {
@@ -223,6 +256,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   }
   __syncthreads();
   constexpr int CPR = CN / 8;  // 16-byte pieces per tile row
+  // (batch, position) of tile row 0; rows advance by 256 / CPR per step
+  const int b0 = m0 / a.S, p0 = m0 % a.S;
   for (int c = tid; c < BM * CPR; c += 256) {
     const int rr = c / CPR, c8 = (c % CPR) * 8;
     const int row = m0 + rr;
@@ -241,7 +276,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
         const bool isk = col < Hq + Hk;
         const int cc = isk ? col - Hq : col - Hq - Hk;
         const int g = cc / a.hd, d = cc % a.hd;
-        const int b = row / a.S, p = a.start_pos + row % a.S;
+        int b = b0, p = p0 + rr;
+        while (p >= a.S) { p -= a.S; ++b; }
+        p += a.start_pos;
         u16 *dst = static_cast<u16 *>(isk ? a.kc : a.vc);
         *reinterpret_cast<uint4 *>(dst + (((int64_t)b * a.cap + p) * a.G + g) * a.hd + d) = val;
       }
