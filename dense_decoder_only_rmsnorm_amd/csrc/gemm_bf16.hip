@@ -195,22 +195,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int CN = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
   constexpr int LDC = CN + 8;
   u16 *Cs = smem;  // [BM][LDC], reuses the operand buffers (loop ended with a barrier)
-  // sequence positions (row % S) of this lane's rows, for the RoPE table:
-  // one division per thread, then wrap-around steps
-  int tpos[EPI == EPI_QKV_ROPE ? FM : 1][16];
-  if (EPI == EPI_QKV_ROPE) {
-    const int pbase = m0 % a.S;  // position of tile row 0
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // tile row of this value, clamped to the last row of the matrix (>= 0: the tile starts inside it)
-        const int x = min(rloc + i * 32 + 8 * (r / 4) + (r % 4), a.M - 1 - m0);
-        int p = pbase + x;
-        while (p >= a.S) p -= a.S;
-        tpos[i][r] = p;
-      }
-  }
+  const int pbase = m0 % a.S;  // sequence position of tile row 0 (RoPE table row = row % S)
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -231,18 +216,29 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
           const bool rot = col < Hq + Hk;
           const int d = (col < Hq ? col : col - Hq) % a.hd;
           const bool odd = col & 1;
-          // the 16 table entries of this block are loaded together (valid
-          // addresses for every lane), then applied
-          float2 cs[16];
+          // table entries are loaded 8 at a time (valid addresses for every
+          // lane), then applied
 #pragma unroll
-          for (int r = 0; r < 16; ++r) cs[r] = a.tab[(int64_t)tpos[i][r] * (a.hd / 2) + d / 2];
+          for (int h = 0; h < 2; ++h) {  // two groups of 8 rows
+            float2 cs[8];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = rloc + i * 32 + 8 * (r / 4) + (r % 4);
-            float v = acc[i][j][r];
-            const float pv = __shfl_xor(v, 1, kWave);
-            if (rot) v = odd ? pv * cs[r].y + v * cs[r].x : v * cs[r].x - pv * cs[r].y;
-            Cs[rr * LDC + ccol] = f2bf(v);
+            for (int q = 0; q < 8; ++q) {
+              const int r = 8 * h + q;
+              // tile row clamped to the matrix (>= 0: the tile starts inside it), then its position
+              const int x = min(rloc + i * 32 + 8 * (r / 4) + (r % 4), a.M - 1 - m0);
+              int p = pbase + x;
+              if (p >= a.S) p = a.S >= BM ? p - a.S : p % a.S;
+              cs[q] = a.tab[(int64_t)p * (a.hd / 2) + d / 2];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const int r = 8 * h + q;
+              const int rr = rloc + i * 32 + 8 * (r / 4) + (r % 4);
+              float v = acc[i][j][r];
+              const float pv = __shfl_xor(v, 1, kWave);
+              if (rot) v = odd ? pv * cs[q].y + v * cs[q].x : v * cs[q].x - pv * cs[q].y;
+              Cs[rr * LDC + ccol] = f2bf(v);
+            }
           }
         } else {
 #pragma unroll
