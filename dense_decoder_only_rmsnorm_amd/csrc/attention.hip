@@ -311,25 +311,44 @@ __global__ __launch_bounds__(256) void attn_fwd_tiled128(AttnArgs a) {
     const u16 *ks = Ks[kt & 1];
     const u16 *vs = Vs[kt & 1];
 
-    // S^T = K Q^T: two 32-key blocks x two 32-query blocks
+    // S^T = K Q^T: two 32-key blocks x two 32-query blocks.  Rows kb*32 + i
+    // of K and 64*wave + 32*qb + i of Q (i = lane % 32) share the swizzle
+    // i & 15; the fragments of head-dim step t+1 are read while the four
+    // MFMAs of step t run.
     f32x16 sc[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[kb][qb][r] = 0.f;
-      const int kr = kb * 32 + (lane & 31);
+    const u16 *krow = ks + (lane & 31) * HD;
+    const u16 *qrow = Qs + (wave * 64 + (lane & 31)) * HD;
+    const int isw = lane & 15;
+    bf16x8 kf[2][2], qf[2][2];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ks + kr * HD + (((2 * t + hf) ^ (kr & 15)) * 8));
+    for (int x = 0; x < 2; ++x) {
+      kf[0][x] = *reinterpret_cast<const bf16x8 *>(krow + x * 32 * HD + ((hf ^ isw) * 8));
+      qf[0][x] = *reinterpret_cast<const bf16x8 *>(qrow + x * 32 * HD + ((hf ^ isw) * 8));
+    }
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int qr = wave * 64 + qb * 32 + (lane & 31);
-          const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(Qs + qr * HD + (((2 * t + hf) ^ (qr & 15)) * 8));
-          sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf, sc[kb][qb], 0, 0, 0);
+    for (int t = 0; t < NT; ++t) {
+      const int cb = t & 1;
+      if (t + 1 < NT) {
+        const int co = ((2 * (t + 1) + hf) ^ isw) * 8;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          kf[cb ^ 1][x] = *reinterpret_cast<const bf16x8 *>(krow + x * 32 * HD + co);
+          qf[cb ^ 1][x] = *reinterpret_cast<const bf16x8 *>(qrow + x * 32 * HD + co);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cb][kb], qf[cb][qb], sc[kb][qb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // online softmax per query, in log2 units.  The running maximum m only
     // moves when a tile's maximum exceeds it by more than 8 (P then stays

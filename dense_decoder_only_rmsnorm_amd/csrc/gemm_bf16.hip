@@ -115,43 +115,70 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) koff[kk] = (((2 * kk + (lane >> 5)) ^ sw) * 8);
 
+  // Two stages.  Chunk kt is computed from stage kt&1 in four k-steps; the
+  // fragments of step kk+1 are read during the MFMAs of step kk.  Within the
+  // last step (its fragments are already in registers) the wave waits for
+  // its loads of chunk kt+1, meets the others at the barrier, refills the
+  // stage it just finished with chunk kt+2 and reads the first fragments of
+  // chunk kt+1: the barrier, the refill and that LDS latency overlap the
+  // step's MFMAs.
   const int KT = K / BK;
+  constexpr int KS = BK / 16;
   issue(0, 0);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) issue(cur ^ 1, (kt + 1) * BK);
-    const u16 *Ab = As + (cur * BM + wm * WM + frow) * RS;
-    const u16 *Bb = Bs + (cur * BN + wn * WN + frow) * RS;
-    bf16x8 af[2][FM], bfr[2][FN];
+  if (KT > 1) issue(1, BK);
+  bf16x8 af[2][FM], bfr[2][FN];
+  {
+    const u16 *Ab = As + (wm * WM + frow) * RS;
+    const u16 *Bb = Bs + (wn * WN + frow) * RS;
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[0][i] = *reinterpret_cast<const bf16x8 *>(Ab + i * 32 * RS + koff[0]);
 #pragma unroll
     for (int j = 0; j < FN; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8 *>(Bb + j * 32 * RS + koff[0]);
+  }
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    const u16 *Ab = As + (cur * BM + wm * WM + frow) * RS;
+    const u16 *Bb = Bs + (cur * BN + wn * WN + frow) * RS;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+    for (int kk = 0; kk < KS; ++kk) {
       const int cb = kk & 1;
-      if (kk + 1 < BK / 16) {
+      // first row block of this step's MFMAs (their fragments are in registers)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][0], bfr[cb][j], acc[0][j], 0, 0, 0);
+      // then the reads for the next step, which overlap the remaining MFMAs
+      // (issued here, a full wait on LDS reads before the first MFMA group
+      // only covers this step's fragments)
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + 1 < KS) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
           af[cb ^ 1][i] = *reinterpret_cast<const bf16x8 *>(Ab + i * 32 * RS + koff[kk + 1]);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           bfr[cb ^ 1][j] = *reinterpret_cast<const bf16x8 *>(Bb + j * 32 * RS + koff[kk + 1]);
+      } else if (kt + 1 < KT) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of chunk kt+1 have landed
+        __syncthreads();                      // everyone's have, and everyone is done reading stage cur
+        if (kt + 2 < KT) issue(cur, (kt + 2) * BK);
+        const u16 *An = As + ((cur ^ 1) * BM + wm * WM + frow) * RS;
+        const u16 *Bn = Bs + ((cur ^ 1) * BN + wn * WN + frow) * RS;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[cb ^ 1][i] = *reinterpret_cast<const bf16x8 *>(An + i * 32 * RS + koff[0]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfr[cb ^ 1][j] = *reinterpret_cast<const bf16x8 *>(Bn + j * 32 * RS + koff[0]);
       }
-      // keep the next step's fragment reads ahead of this step's MFMAs (the
-      // scheduler would otherwise sink each read next to its use and expose
-      // the LDS latency once per MFMA group)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 1; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();  // the next stage has landed (waits for this wave's loads) and this one is free
   }
+  __syncthreads();  // every wave is done with the stages before the epilogue reuses them
 
   // ---------------- epilogue ----------------
   const int col_l = lane & 31;
