@@ -7,21 +7,24 @@
 // carrying ~16 significant bits; both planes are multiplied against the same
 // weight fragment (two MFMAs), so the weight bytes do not change.
 //
-// A block of 256 threads owns 64 B-rows (four 16-column MFMA blocks, one per
-// wave) and one K slice (grid.y).  The K slice streams through three LDS
-// stages of 64 k: weights and both activation planes arrive with
-// global_load_lds_dwordx4 in fully coalesced 1 KB pieces (8 rows x 128
-// bytes), stored with the 16-byte chunk swizzle c ^ ((row >> 1) & 7) so the
-// MFMA fragment reads of 16 consecutive rows are bank-conflict free.  Loading
-// fragments straight from global memory in MFMA layout would make every
-// quarter-wave touch 16 different rows.  The activations are shared by the
-// four waves through LDS.  MFMA 16x16x32 (v_mfma_f32_16x16x32_bf16): lane l
-// supplies row/column (l % 16) and eight consecutive k at 8*(l / 16); output
-// register r of lane l holds row 4*(l/16) + r, column l % 16.
+// A block of 512 threads owns 64 B-rows and one K slice (grid.y).  The K
+// slice streams through two LDS stages of 64 k: weights and both activation
+// planes arrive with global_load_lds_dwordx4 in fully coalesced 1 KB pieces
+// (8 rows x 128 bytes), stored with the 16-byte chunk swizzle
+// c ^ ((row >> 1) & 7) so the MFMA fragment reads of 16 consecutive rows are
+// bank-conflict free.  The activations are shared by all waves through LDS.
+// Waves w and w+4 own the same 16 B-rows and split each 64-k stage into its
+// two 32-k halves; their partial sums meet in LDS at the end.  Small stages
+// and eight waves per block leave room for three blocks per compute unit:
+// the weight stream is latency-bound, and resident waves, more than a deeper
+// pipeline per block, are what keep enough loads in flight.
+// MFMA 16x16x32 (v_mfma_f32_16x16x32_bf16): lane l supplies row/column
+// (l % 16) and eight consecutive k at 8*(l / 16); output register r of lane
+// l holds row 4*(l/16) + r, column l % 16.
 //
 // Epilogues:
 //   SK_PARTIAL       fp32 split-K partial [ks][M][N] (summed by the consumer)
-//   SK_SWIGLU_HILO   B-rows interleave w1/w3 (32 each per block);
+//   SK_SWIGLU_HILO   B-rows interleave w1/w3 (16 each, twice per block);
 //                    u = silu(gate) * up written as hi/lo planes [P2 3.5]
 //   SK_SWIGLU_BF16   same, one bf16 plane
 //   SK_LOGITS        fp32 logits (optional) + per-block (max, argmax)
@@ -34,15 +37,16 @@ namespace llk {
 namespace {
 
 constexpr int SK_KCH = 64;     // k per LDS stage
-constexpr int SK_STAGES = 3;
+constexpr int SK_STAGES = 2;
 constexpr int SK_ROWB = SK_KCH * 2;  // bytes per tile row (128)
 
 template <int MB, int EPI>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
+__global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a) {
   // stage layout (bf16): A hi [64][64], A lo [64][64], B [64][64]
   constexpr int ST_ELEMS = 3 * 64 * SK_KCH;
   extern __shared__ __align__(16) u16 sm[];  // [SK_STAGES][ST_ELEMS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wcol = wave & 3, khalf = wave >> 2;
   const int nblk0 = blockIdx.x;
   const int ks = blockIdx.y;
   const int Kc = a.K / a.ksplit;
@@ -50,15 +54,15 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
   const int nchunk = Kc / SK_KCH;
 
   // Loader: 24 pieces of 1 KB per stage (A hi 8, A lo 8, B 8); wave w issues
-  // pieces w, w+4, ...  Piece p covers tile rows 8*(p%8) .. +7 of its matrix;
+  // pieces w, w+8, w+16.  Piece p covers tile rows 8*(p%8) .. +7 of its matrix;
   // lane L -> row 8*(p%8) + L/8, physical chunk L%8 holding logical chunk
   // (L%8) ^ ((row >> 1) & 7).  Rows past M or past the weight read a clamped
   // valid row: they only feed outputs that are never stored.
   const int lr = lane >> 3, lq = lane & 7;
-  const u16 *src[6];
+  const u16 *src[3];
 #pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    const int p = wave + 4 * i;        // 0..23
+  for (int i = 0; i < 3; ++i) {
+    const int p = wave + 8 * i;        // 0..23
     const int mat = p >> 3;            // 0: A hi, 1: A lo, 2: B
     const int row = (p & 7) * 8 + lr;  // tile row 0..63
     const int c = lq ^ ((row >> 1) & 7);
@@ -94,8 +98,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
   auto issue = [&](int stage, int chunk) {
     u16 *st = sm + stage * ST_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int p = __builtin_amdgcn_readfirstlane(wave + 4 * i);
+    for (int i = 0; i < 3; ++i) {
+      const int p = __builtin_amdgcn_readfirstlane(wave + 8 * i);
       u16 *dst = st + (p >> 3) * 64 * SK_KCH + (p & 7) * 8 * SK_KCH;
       __builtin_amdgcn_global_load_lds((const void *)(src[i] + chunk * SK_KCH),
                                        (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
@@ -110,22 +114,16 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
   for (int i = 0; i < MB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   issue(0, 0);
-  if (nchunk > 1) issue(1, 1);
   for (int ch = 0; ch < nchunk; ++ch) {
-    // wait for this wave's pieces of stage ch (the later stage may stay in flight)
-    if (ch + 1 < nchunk)
-      __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): one later stage of 6 loads outstanding
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    // every wave's pieces of this stage are in LDS, and every wave is done
-    // reading the stage that the next issue overwrites.  (A plain
-    // __syncthreads would also wait for the stage still in flight.)
+    // this wave's pieces of stage ch have landed; after the barrier every
+    // wave's have, and every wave is done reading the stage refilled next
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    if (ch + 2 < nchunk) issue((ch + 2) % SK_STAGES, ch + 2);
+    if (ch + 1 < nchunk) issue((ch + 1) % SK_STAGES, ch + 1);
     const u16 *st = sm + (ch % SK_STAGES) * ST_ELEMS;
-    const u16 *bp = st + 2 * 64 * SK_KCH + (wave * 16 + frow) * SK_KCH;
-#pragma unroll
-    for (int kk = 0; kk < SK_KCH / 32; ++kk) {
+    const u16 *bp = st + 2 * 64 * SK_KCH + (wcol * 16 + frow) * SK_KCH;
+    {
+      const int kk = khalf;  // this wave's 32-k half of the stage
       const int co = ((4 * kk + (lane >> 4)) ^ sw) * 8;
       const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(bp + co);
 #pragma unroll
@@ -140,25 +138,35 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
   }
   __syncthreads();  // stages are reused for the epilogue
 
-  // wave w holds column block w: acc[mb][r] = C[mb*16 + 4*(lane/16) + r][16w + lane%16]
+  // wave pair (w, w+4) holds column block w%4: acc[mb][r] = partial
+  // C[mb*16 + 4*(lane/16) + r][16*(w%4) + lane%16] over its k halves
   float *red = reinterpret_cast<float *>(sm);  // [MB*16 rows][64 cols]
+  if (khalf == 0) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[(mb * 16 + 4 * (lane >> 4) + r) * 64 + wave * 16 + frow] = acc[mb][r];
+      for (int r = 0; r < 4; ++r) red[(mb * 16 + 4 * (lane >> 4) + r) * 64 + wcol * 16 + frow] = acc[mb][r];
+  }
+  __syncthreads();
+  if (khalf == 1) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(mb * 16 + 4 * (lane >> 4) + r) * 64 + wcol * 16 + frow] += acc[mb][r];
+  }
   __syncthreads();
   constexpr int ROWS = MB * 16;
 
   if (EPI == SK_PARTIAL) {
     float *C = static_cast<float *>(a.C) + (int64_t)ks * a.c_plane;
-    for (int e = tid; e < ROWS * 64; e += 256) {
+    for (int e = tid; e < ROWS * 64; e += 512) {
       const int row = e >> 6, col = nblk0 * 64 + (e & 63);
       if (row < a.M && col < a.N) C[(int64_t)row * a.N + col] = red[e];
     }
   } else if (EPI == SK_SWIGLU_HILO || EPI == SK_SWIGLU_BF16) {
     const int F = a.N / 2;
     u16 *C = static_cast<u16 *>(a.C);
-    for (int e = tid; e < ROWS * 32; e += 256) {
+    for (int e = tid; e < ROWS * 32; e += 512) {
       const int row = e >> 5, uc = e & 31;
       const int gc = (uc >> 4) * 32 + (uc & 15);  // gate column in the tile; up is 16 further
       const int col = nblk0 * 32 + uc;
@@ -178,7 +186,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
     }
   } else {  // SK_LOGITS
     if (a.logits) {
-      for (int e = tid; e < ROWS * 64; e += 256) {
+      for (int e = tid; e < ROWS * 64; e += 512) {
         const int row = e >> 6, col = nblk0 * 64 + (e & 63);
         if (row < a.M && col < a.N) a.logits[(int64_t)row * a.N + col] = red[e];
       }
@@ -206,7 +214,7 @@ hipError_t launch_one(const SkinnyArgs &a, dim3 grid, size_t lds, hipStream_t s)
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny_kernel<MB, EPI>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   (void)attr;
-  hipLaunchKernelGGL((skinny_kernel<MB, EPI>), grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL((skinny_kernel<MB, EPI>), grid, dim3(512), lds, s, a);
   return hipGetLastError();
 }
 
