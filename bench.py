@@ -18,6 +18,7 @@ pass of K steps (llama_timing_enable), so the headline timing carries no
 instrumentation.
 """
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -29,6 +30,30 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+# HBM bytes per launch of the roofline kernels, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs (see the summary beside it); each entry records the
+# SHA-256 of the sources it was measured with
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary,
+    or None when there is none or its sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entry = json.load(f)["kernels"][kernel]
+    except (OSError, ValueError, KeyError):
+        return None
+    h = hashlib.sha256()
+    for rel in entry["sources"]:
+        try:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        except OSError:
+            return None
+    if h.hexdigest() != entry["sources_sha256"]:
+        return None
+    return float(entry["bytes_per_launch"])
 
 
 def log(*a):
@@ -211,7 +236,8 @@ def main():
         out["prefill"] = dict(ms=ms, tok_s=B * S / (ms / 1e3), step_tflops=total_flop / (ms / 1e3) / 1e12,
                               roofline={"kernel": "gemm_w1w3_swiglu", "bound": "mfma", "achieved": round(ach, 2),
                                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                        "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                        "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                                        "traffic": measured_traffic("gemm_w1w3_swiglu"),
                                         "flop_per_launch": flop, "avg_launch_ms": dk["avg_ms"]})
         del ws, logits, ids
         torch.cuda.empty_cache()
@@ -257,7 +283,8 @@ def main():
                              step_frac=step_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
                              roofline={"kernel": "attn_decode", "bound": "hbm", "achieved": round(ach, 1),
                                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                                       "traffic": None, "bytes_per_launch": kv_bytes, "avg_launch_ms": dk["avg_ms"]})
+                                       "traffic": measured_traffic("attn_decode"), "bytes_per_launch": kv_bytes,
+                                       "avg_launch_ms": dk["avg_ms"]})
         del caches, kvs, ws
         torch.cuda.empty_cache()
 
