@@ -465,6 +465,220 @@ __global__ __launch_bounds__(256) void attn_fwd_tiled128(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Prefill, bf16, head_dim 128, eight waves: the same block of 256 query rows
+// of one KV group and the same K/V tile pipeline as attn_fwd_tiled128, but
+// each wave owns 32 query rows with its Q fragments in registers.  Two waves
+// share each SIMD, so one wave's softmax (vector ALU, exp) runs while the
+// other's MFMAs do, instead of one wave alternating between them.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
+  constexpr int HD = 128;
+  constexpr int KT = 64;            // keys per tile
+  constexpr int TILE = KT * HD;     // elements per K or V tile
+  constexpr int NT = HD / 16;       // S^T k-steps over head_dim
+  constexpr int NO = HD / 32;       // O^T row blocks over head_dim
+  __shared__ __align__(16) u16 Ks[2][TILE];
+  __shared__ __align__(16) u16 Vs[2][TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;  // 8 waves
+  const int n_rep = a.H / a.G;
+  const int QB = 256 / n_rep;  // positions per block
+  const int nq = (a.S + QB - 1) / QB;
+  const int L = blockIdx.x;
+  const int g = L % a.G;
+  const int rest = L / a.G;
+  const int b = rest % a.B;
+  const int qblk = nq - 1 - rest / a.B;
+
+  const int hf = lane >> 5;  // half of the wave
+  const int rho = wave * 32 + (lane & 31);
+  const int hq = g * n_rep + rho / QB;
+  const int sq = qblk * QB + rho % QB;
+  const bool valid = sq < a.S;
+  const int srow = valid ? sq : a.S - 1;
+  const int qpos = a.start_pos + srow;
+  const int wmax = (int)wave_max((float)qpos);
+  const int wmin = -(int)wave_max((float)-qpos);
+
+  // Q fragments (B operand of S^T = K Q^T): row rho, head-dim 16t + 8*hf .. +7
+  bf16x8 qf[NT];
+  {
+    const u16 *qrow = static_cast<const u16 *>(a.q) + (int64_t)(b * a.S + srow) * a.q_stride + hq * HD + 8 * hf;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) qf[t] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * t);
+  }
+
+  const int last_s = min(a.S, (qblk + 1) * QB) - 1;
+  const int kv_end = a.start_pos + last_s + 1;  // keys [0, kv_end)
+  const int ntiles = (kv_end + KT - 1) / KT;
+  const int64_t kstride = (int64_t)a.G * HD;
+  const u16 *Kg = static_cast<const u16 *>(a.k) + ((int64_t)b * a.kcap * a.G + g) * HD;
+  const u16 *Vg = static_cast<const u16 *>(a.v) + ((int64_t)b * a.kcap * a.G + g) * HD;
+
+  // loader: piece p = wave + 8i (i < 2) covers tile rows 4p .. 4p+3; lane L
+  // -> row 4p + L/16, physical chunk L%16.  K keeps logical chunk
+  // (L%16) ^ (row & 15) there, V (L%16) ^ vswz(row), vswz(r) =
+  // ((r & 3) << 2) | ((r >> 2) & 3), matched to its transposed reads.
+  int lrow[2], lcol[2], lcolv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = wave + 8 * i;
+    lrow[i] = 4 * p + (lane >> 4);
+    lcol[i] = ((lane & 15) ^ (lrow[i] & 15)) * 8;
+    lcolv[i] = ((lane & 15) ^ (((lrow[i] & 3) << 2) | ((lrow[i] >> 2) & 3))) * 8;
+  }
+  auto issue = [&](int kt, int buf) {
+    const int k0 = kt * KT;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int key = min(k0 + lrow[i], kv_end - 1);  // rows past the end are masked
+      const int p = __builtin_amdgcn_readfirstlane(wave + 8 * i);
+      __builtin_amdgcn_global_load_lds((const void *)(Kg + (int64_t)key * kstride + lcol[i]),
+                                       (__attribute__((address_space(3))) void *)(Ks[buf] + p * 4 * HD), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(Vg + (int64_t)key * kstride + lcolv[i]),
+                                       (__attribute__((address_space(3))) void *)(Vs[buf] + p * 4 * HD), 16, 0, 0);
+    }
+  };
+
+  f32x16 o[NO];
+#pragma unroll
+  for (int i = 0; i < NO; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const float c = a.scale * kLog2e;
+
+  // V^T fragments (tr16 reads): 16-lane group G reads rows 4*hf + j/4 (+8)
+  // of a 16-key step at columns 32*ob + 16*(G&1) + 4*(j&3); lane j then
+  // holds V[4 keys][d], d = 32*ob + lane%32
+  const int jj = lane & 15, dg = (lane >> 4) & 1;
+  const int vr0 = 4 * hf + (jj >> 2);
+  const int vq = 2 * dg + ((jj & 3) >> 1), vhalf = (jj & 1) * 4;
+
+  auto tile = [&](int kt, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    const int k0 = kt * KT;
+    const u16 *ks = Ks[kt & 1];
+    const u16 *vs = Vs[kt & 1];
+    // S^T = K Q^T: two 32-key blocks; K rows kb*32 + lane%32
+    f32x16 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+    const u16 *krow = ks + (lane & 31) * HD;
+    const int isw = lane & 15;
+    bf16x8 kf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) kf[0][kb] = *reinterpret_cast<const bf16x8 *>(krow + kb * 32 * HD + ((hf ^ isw) * 8));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int cb = t & 1;
+      if (t + 1 < NT) {
+        const int co = ((2 * (t + 1) + hf) ^ isw) * 8;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) kf[cb ^ 1][kb] = *reinterpret_cast<const bf16x8 *>(krow + kb * 32 * HD + co);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cb][kb], qf[t], sc[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // online softmax of this lane's query, log2 units, lazy rescale (the
+    // running maximum moves only when a tile exceeds it by more than 8)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (MASK) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key > qpos) sc[kb][r] = -INFINITY;
+        }
+        mx = fmaxf(mx, sc[kb][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
+      const float m_new = fmaxf(m, mx);  // finite: key 0 is visible to every query
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+      m = m_new;
+#pragma unroll
+      for (int i = 0; i < NO; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -m));
+        sc[kb][r] = p;
+        rs += p;
+      }
+    l += rs + __shfl_xor(rs, 32, kWave);
+    // O^T += V^T P^T over four 16-key steps
+#pragma unroll
+    for (int ksp = 0; ksp < 4; ++ksp) {
+      const int kb = ksp >> 1, t = ksp & 1;
+      bf16x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sc[kb][8 * t + e];
+      const int rbase = 16 * ksp + vr0;
+#pragma unroll
+      for (int ob = 0; ob < NO; ++ob) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        u32x2 wv[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int r = rbase + 8 * h2;
+          const int vsw = ((r & 3) << 2) | ((r >> 2) & 3);
+          const int off = (r * HD + (((4 * ob + vq) ^ vsw) * 8) + vhalf) * (int)sizeof(u16);
+          const v4s w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s *)((__attribute__((address_space(3))) const char *)vs + off));
+          wv[h2] = __builtin_bit_cast(u32x2, w);
+        }
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(wv[0].x, wv[0].y, wv[1].x, wv[1].y));
+        o[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[ob], 0, 0, 0);
+      }
+    }
+  };
+
+  // tiles [0, nfull) are visible to every query of this wave; the rest are
+  // masked, and tiles past the wave's last query are skipped.  Every wave
+  // passes the same ntiles barriers.
+  const int nfull = min(ntiles, (wmin + 1) / KT);
+  issue(0, 0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    __syncthreads();  // tile kt has landed; every wave is done with tile kt-1
+    if (kt + 1 < ntiles) issue(kt + 1, (kt + 1) & 1);
+    if (kt < nfull)
+      tile(kt, std::integral_constant<bool, false>());
+    else if (kt * KT <= wmax)
+      tile(kt, std::integral_constant<bool, true>());
+  }
+
+  // lane holds O^T[d = 32*ob + 8*(r/4) + 4*hf + r%4][query lane%32]
+  if (valid) {
+    const float inv = 1.0f / l;
+    u16 *orow = static_cast<u16 *>(a.o) + (int64_t)(b * a.S + srow) * a.q_stride + hq * HD;
+#pragma unroll
+    for (int ob = 0; ob < NO; ++ob)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = ob * 32 + 8 * q4 + 4 * hf;
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(o[ob][q4 * 4 + 0] * inv) | ((uint32_t)f2bf(o[ob][q4 * 4 + 1] * inv) << 16);
+        pk.y = (uint32_t)f2bf(o[ob][q4 * 4 + 2] * inv) | ((uint32_t)f2bf(o[ob][q4 * 4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2 *>(orow + d) = pk;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Prefill, fp32 (one wave per block, one query per lane)
 // ---------------------------------------------------------------------------
 template <int HD>
@@ -1024,7 +1238,11 @@ hipError_t prefill_hd(int dtype, const AttnArgs &a, hipStream_t s) {
   if (dtype == 1 && HD == 128) {
     const int QB = 256 / (a.H / a.G);
     const int nblk = ((a.S + QB - 1) / QB) * a.G * a.B;
+#ifdef ATTN_TILED4
     hipLaunchKernelGGL(attn_fwd_tiled128, dim3(nblk), dim3(256), 0, s, a);
+#else
+    hipLaunchKernelGGL(attn_fwd_w8, dim3(nblk), dim3(512), 0, s, a);
+#endif
   } else if (dtype == 1) {
     const int QB = 128 / (a.H / a.G);
     dim3 grid((a.S + QB - 1) / QB, a.G, a.B);
