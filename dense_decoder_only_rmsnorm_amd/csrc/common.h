@@ -14,13 +14,10 @@ typedef uint16_t u16;
 constexpr int kWave = 64;
 
 // bf16 <-> fp32.  Storage is raw uint16 bit patterns; widening is exact,
-// narrowing rounds to nearest even (inputs are finite).
+// narrowing rounds to nearest even (the hardware conversion, one instruction
+// on gfx950; inputs are finite).
 __device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float(((uint32_t)b) << 16); }
-__device__ __forceinline__ u16 f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (u16)(u >> 16);
-}
+__device__ __forceinline__ u16 f2bf(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
 // Split v into hi + lo, both bf16, with hi = bf16(v) and lo = bf16(v - hi):
 // hi + lo carries about 16 significant bits of v.
 __device__ __forceinline__ void split_hilo(float v, u16 &hi, u16 &lo) {

@@ -225,6 +225,24 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const int pbase = m0 % a.S;  // sequence position of tile row 0 (RoPE table row = row % S)
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    // QKV: table row offsets of this lane's 16 rows in row block i (shared by
+    // all its column blocks).  Rows past the matrix are clamped to its last
+    // row so every lookup stays inside the table; their values are not stored.
+    int toff[16];
+    if (EPI == EPI_QKV_ROPE) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int x = min(rloc + i * 32 + 8 * (r / 4) + (r % 4), a.M - 1 - m0);
+        int p = pbase + x;
+        // sequences of at least BM rows wrap at most once within a tile (a
+        // select); shorter ones take the (uniform) modulo path
+        if (a.S >= BM)
+          p = p >= a.S ? p - a.S : p;
+        else
+          p %= a.S;
+        toff[r] = p * (a.hd / 2);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       if (EPI == EPI_SWIGLU) {
@@ -237,35 +255,25 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
         }
       } else {
         const int ccol = wn * WN + j * 32 + col_l;
-        if (EPI == EPI_QKV_ROPE) {
-          const int col = n0 + ccol;
-          const int Hq = a.H * a.hd, Hk = a.G * a.hd;
-          const bool rot = col < Hq + Hk;
-          const int d = (col < Hq ? col : col - Hq) % a.hd;
-          const bool odd = col & 1;
-          // table entries are loaded 8 at a time (valid addresses for every
-          // lane), then applied
+        // A 32-column block lies inside one head of one of q, k, v (the head
+        // size is a multiple of 32, checked at launch), so whether it rotates
+        // and its first head dimension are the same for the whole wave.
+        const int col0 = n0 + wn * WN + j * 32;
+        const int Hq = a.H * a.hd, Hk = a.G * a.hd;
+        if (EPI == EPI_QKV_ROPE && col0 < Hq + Hk) {
+          const int dh = (((col0 < Hq ? col0 : col0 - Hq) % a.hd) + col_l) >> 1;  // table column
+          // pair (2t, 2t+1) sits in lanes (2t, 2t+1) of one row:
+          //   even: x0 cos - x1 sin,  odd: x1 cos + x0 sin
+          const float sgn = (lane & 1) ? 1.f : -1.f;
+          float2 cs[16];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {  // two groups of 8 rows
-            float2 cs[8];
+          for (int r = 0; r < 16; ++r) cs[r] = a.tab[toff[r] + dh];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const int r = 8 * h + q;
-              // tile row clamped to the matrix (>= 0: the tile starts inside it), then its position
-              const int x = min(rloc + i * 32 + 8 * (r / 4) + (r % 4), a.M - 1 - m0);
-              int p = pbase + x;
-              if (p >= a.S) p = a.S >= BM ? p - a.S : p % a.S;
-              cs[q] = a.tab[(int64_t)p * (a.hd / 2) + d / 2];
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const int r = 8 * h + q;
-              const int rr = rloc + i * 32 + 8 * (r / 4) + (r % 4);
-              float v = acc[i][j][r];
-              const float pv = __shfl_xor(v, 1, kWave);
-              if (rot) v = odd ? pv * cs[q].y + v * cs[q].x : v * cs[q].x - pv * cs[q].y;
-              Cs[rr * LDC + ccol] = f2bf(v);
-            }
+          for (int r = 0; r < 16; ++r) {
+            const int rr = rloc + i * 32 + 8 * (r / 4) + (r % 4);
+            const float v = acc[i][j][r];
+            const float pv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+            Cs[rr * LDC + ccol] = f2bf(fmaf(pv, sgn * cs[r].y, v * cs[r].x));
           }
         } else {
 #pragma unroll
@@ -279,37 +287,44 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   }
   __syncthreads();
   constexpr int CPR = CN / 8;  // 16-byte pieces per tile row
-  // (batch, position) of tile row 0; rows advance by 256 / CPR per step
-  const int b0 = m0 / a.S, p0 = m0 % a.S;
-  for (int c = tid; c < BM * CPR; c += 256) {
-    const int rr = c / CPR, c8 = (c % CPR) * 8;
-    const int row = m0 + rr;
-    if (row >= a.M) continue;
-    const uint4 val = *reinterpret_cast<const uint4 *>(Cs + rr * LDC + c8);
-    if (EPI == EPI_SWIGLU) {
-      const int ucol = n0 / 2 + c8;
-      if (ucol < a.N / 2) *reinterpret_cast<uint4 *>(static_cast<u16 *>(a.C) + (int64_t)row * a.ldc + ucol) = val;
-    } else if (EPI == EPI_QKV_ROPE) {
-      const int col = n0 + c8;
-      if (col >= a.N) continue;
-      const int Hq = a.H * a.hd, Hk = a.G * a.hd;
-      if (col < Hq) {
-        *reinterpret_cast<uint4 *>(a.q + (int64_t)row * Hq + col) = val;
-      } else {
-        const bool isk = col < Hq + Hk;
-        const int cc = isk ? col - Hq : col - Hq - Hk;
-        const int g = cc / a.hd, d = cc % a.hd;
-        int b = b0, p = p0 + rr;
-        while (p >= a.S) { p -= a.S; ++b; }
-        p += a.start_pos;
-        u16 *dst = static_cast<u16 *>(isk ? a.kc : a.vc);
-        *reinterpret_cast<uint4 *>(dst + (((int64_t)b * a.cap + p) * a.G + g) * a.hd + d) = val;
-      }
-    } else {
-      const int col = n0 + c8;
-      if (col < a.N) *reinterpret_cast<uint4 *>(static_cast<u16 *>(a.C) + (int64_t)row * a.ldc + col) = val;
+  static_assert(256 % CPR == 0, "a thread keeps one column piece for the whole copy");
+  // Each thread copies the same 8 columns of every (256 / CPR)-th row, so
+  // everything that depends on the column is computed once.
+  const int c8 = (tid % CPR) * 8;
+  const int col = (EPI == EPI_SWIGLU ? n0 / 2 : n0) + c8;
+  if (col >= (EPI == EPI_SWIGLU ? a.N / 2 : a.N)) return;
+  if (EPI == EPI_QKV_ROPE) {
+    const int Hq = a.H * a.hd, Hk = a.G * a.hd;
+    if (col < Hq) {
+      for (int rr = tid / CPR; rr < BM && m0 + rr < a.M; rr += 256 / CPR)
+        *reinterpret_cast<uint4 *>(a.q + (int64_t)(m0 + rr) * Hq + col) =
+            *reinterpret_cast<const uint4 *>(Cs + rr * LDC + c8);
+      return;
     }
+    // k or v: row m0 + rr is (batch b, position p) of the cache
+    const bool isk = col < Hq + Hk;
+    const int cc = isk ? col - Hq : col - Hq - Hk;
+    const int g = cc / a.hd, d = cc % a.hd;
+    u16 *dst = static_cast<u16 *>(isk ? a.kc : a.vc) + (int64_t)g * a.hd + d;
+    const int b0 = m0 / a.S, p0 = m0 % a.S;
+    for (int rr = tid / CPR; rr < BM && m0 + rr < a.M; rr += 256 / CPR) {
+      int b = b0, p = p0 + rr;
+      if (a.S >= BM) {  // at most one wrap within a tile (selects)
+        const bool w = p >= a.S;
+        p = w ? p - a.S : p;
+        b = w ? b + 1 : b;
+      } else {
+        b += p / a.S;
+        p %= a.S;
+      }
+      *reinterpret_cast<uint4 *>(dst + ((int64_t)b * a.cap + p + a.start_pos) * a.G * a.hd) =
+          *reinterpret_cast<const uint4 *>(Cs + rr * LDC + c8);
+    }
+    return;
   }
+  u16 *C = static_cast<u16 *>(a.C) + col;
+  for (int rr = tid / CPR; rr < BM && m0 + rr < a.M; rr += 256 / CPR)
+    *reinterpret_cast<uint4 *>(C + (int64_t)(m0 + rr) * a.ldc) = *reinterpret_cast<const uint4 *>(Cs + rr * LDC + c8);
 }
 
 template <int BM, int BN, int EPI>
@@ -336,7 +351,9 @@ hipError_t launch_gemm_bf16(int epi, const GemmArgs &a, hipStream_t s) {
   switch (epi) {
     case EPI_STORE_F32: return launch_epi<EPI_STORE_F32>(a, s);
     case EPI_RESID: return launch_epi<EPI_RESID>(a, s);
-    case EPI_QKV_ROPE: return launch_epi<EPI_QKV_ROPE>(a, s);
+    case EPI_QKV_ROPE:
+      if (a.hd % 32) return hipErrorInvalidValue;  // the epilogue takes 32-column blocks inside one head
+      return launch_epi<EPI_QKV_ROPE>(a, s);
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, s);
     case EPI_STORE_BF16: return launch_epi<EPI_STORE_BF16>(a, s);
   }
