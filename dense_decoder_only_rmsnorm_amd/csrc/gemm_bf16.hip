@@ -22,6 +22,7 @@
 // consecutive k at 8*(l / 32); B likewise for output column (l % 32).  Output
 // register r of lane l holds row 8*(r/4) + 4*(l/32) + (r%4), column l % 32.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -84,6 +85,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     }
     bsrc[i] = base + (int64_t)min(wr, nrows - 1) * a.ldb + c * 8;
   }
+  // one load instruction of a stage refill: l < AI for A, then B
+  auto issue_one = [&](int stage, int k0, int l) {
+    if (l < AI) {
+      const int j = __builtin_amdgcn_readfirstlane(wave * AI + l);
+      __builtin_amdgcn_global_load_lds((const void *)(asrc[l] + k0),
+                                       (__attribute__((address_space(3))) void *)(As + stage * BM * RS + j * 8 * RS), 16, 0, 0);
+    } else {
+      const int j = __builtin_amdgcn_readfirstlane(wave * BI + (l - AI));
+      __builtin_amdgcn_global_load_lds((const void *)(bsrc[l - AI] + k0),
+                                       (__attribute__((address_space(3))) void *)(Bs + stage * BN * RS + j * 8 * RS), 16, 0, 0);
+    }
+  };
   auto issue = [&](int stage, int k0) {
     u16 *ad = As + stage * BM * RS;
     u16 *bd = Bs + stage * BN * RS;
@@ -116,12 +129,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   for (int kk = 0; kk < BK / 16; ++kk) koff[kk] = (((2 * kk + (lane >> 5)) ^ sw) * 8);
 
   // Two stages.  Chunk kt is computed from stage kt&1 in four k-steps; the
-  // fragments of step kk+1 are read during the MFMAs of step kk.  Within the
-  // last step (its fragments are already in registers) the wave waits for
-  // its loads of chunk kt+1, meets the others at the barrier, refills the
-  // stage it just finished with chunk kt+2 and reads the first fragments of
-  // chunk kt+1: the barrier, the refill and that LDS latency overlap the
-  // step's MFMAs.
+  // fragments of step kk+1 are read during the MFMAs of step kk.  In the last
+  // step of a chunk the wave waits for its loads of chunk kt+1, meets the
+  // others at the barrier, and then refills the stage it just finished with
+  // chunk kt+2 while it runs the step's remaining MFMAs: the refill loads and
+  // the first fragment reads of chunk kt+1 are spread between those MFMAs, so
+  // the address unit drains them while the matrix core stays busy.
   const int KT = K / BK;
   constexpr int KS = BK / 16;
   issue(0, 0);
@@ -136,20 +149,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8 *>(Bb + j * 32 * RS + koff[0]);
   }
-  for (int kt = 0; kt < KT; ++kt) {
+  auto run_chunk = [&](int kt, auto boundary) {
+    constexpr bool BOUNDARY = decltype(boundary)::value;
     const int cur = kt & 1;
     const u16 *Ab = As + (cur * BM + wm * WM + frow) * RS;
     const u16 *Bb = Bs + (cur * BN + wn * WN + frow) * RS;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int cb = kk & 1;
-      // first row block of this step's MFMAs (their fragments are in registers)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][0], bfr[cb][j], acc[0][j], 0, 0, 0);
-      // then the reads for the next step, which overlap the remaining MFMAs
-      // (issued here, a full wait on LDS reads before the first MFMA group
-      // only covers this step's fragments)
       __builtin_amdgcn_sched_barrier(0);
       if (kk + 1 < KS) {
 #pragma unroll
@@ -158,18 +168,34 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           bfr[cb ^ 1][j] = *reinterpret_cast<const bf16x8 *>(Bb + j * 32 * RS + koff[kk + 1]);
-      } else if (kt + 1 < KT) {
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (BOUNDARY) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of chunk kt+1 have landed
         __syncthreads();                      // everyone's have, and everyone is done reading stage cur
-        if (kt + 2 < KT) issue(cur, (kt + 2) * BK);
+        // Refill (past the last chunk the last chunk is loaded again into
+        // this dead stage, which keeps the step free of branches), spread
+        // between the step's remaining MFMAs together with the first
+        // fragment reads of chunk kt+1.
+        const int k0 = min(kt + 2, KT - 1) * BK;
         const u16 *An = As + ((cur ^ 1) * BM + wm * WM + frow) * RS;
         const u16 *Bn = Bs + ((cur ^ 1) * BN + wn * WN + frow) * RS;
+        constexpr int NM = (FM - 1) * FN, NL = AI + BI, NR = FM + FN;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[cb ^ 1][i] = *reinterpret_cast<const bf16x8 *>(An + i * 32 * RS + koff[0]);
+        for (int q = 0; q < NM; ++q) {
+          const int i = 1 + q / FN, j = q % FN;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bfr[cb ^ 1][j] = *reinterpret_cast<const bf16x8 *>(Bn + j * 32 * RS + koff[0]);
+          for (int l = q * NL / NM; l < (q + 1) * NL / NM; ++l) issue_one(cur, k0, l);
+#pragma unroll
+          for (int r = q * NR / NM; r < (q + 1) * NR / NM; ++r) {
+            if (r < FM) af[cb ^ 1][r] = *reinterpret_cast<const bf16x8 *>(An + r * 32 * RS + koff[0]);
+            else bfr[cb ^ 1][r - FM] = *reinterpret_cast<const bf16x8 *>(Bn + (r - FM) * 32 * RS + koff[0]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        continue;
       }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 1; i < FM; ++i)
 #pragma unroll
@@ -177,7 +203,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  for (int kt = 0; kt + 1 < KT; ++kt) run_chunk(kt, std::true_type{});
+  run_chunk(KT - 1, std::false_type{});
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the refill of the dead stage has landed before LDS is reused
   __syncthreads();  // every wave is done with the stages before the epilogue reuses them
 
   // ---------------- epilogue ----------------
