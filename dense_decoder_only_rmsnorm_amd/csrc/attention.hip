@@ -1205,20 +1205,40 @@ __global__ __launch_bounds__(((HD + 63) / 64) * 64) void attn_combine_kernel(Dec
     ms = dot * a.scale * kLog2e;
     vself = a.vnew[kv];
   }
-  float M = ms;
-  for (int c = 0; c < a.nchunk; ++c) M = fmaxf(M, a.pm[base + c]);
-  float L = 0.f, acc = 0.f;
+  // The chunk partials are merged 16 at a time: each group's loads (clamped
+  // to a valid chunk; the extra ones are skipped) are issued together, and
+  // the running maximum M rescales what earlier groups summed.
+  float M = ms, L = 0.f, acc = 0.f;
   if (a.knew) {
-    const float w = exp2f(ms - M);
-    L = w;
-    acc = w * vself;
+    L = 1.f;
+    acc = vself;
   }
-  for (int c = 0; c < a.nchunk; ++c) {
-    const float mc = a.pm[base + c];
-    if (mc == -INFINITY) continue;
-    const float w = exp2f(mc - M);
-    L += w * a.pl[base + c];
-    acc += w * a.po[(base + c) * HD + d];
+  constexpr int CG = 16;
+  for (int c0 = 0; c0 < a.nchunk; c0 += CG) {
+    float pm[CG], pl[CG], po[CG];
+#pragma unroll
+    for (int u = 0; u < CG; ++u) {
+      const int64_t c = base + min(c0 + u, a.nchunk - 1);
+      pm[u] = a.pm[c];
+      pl[u] = a.pl[c];
+      po[u] = a.po[c * HD + d];
+    }
+    float Mg = M;
+#pragma unroll
+    for (int u = 0; u < CG; ++u)
+      if (c0 + u < a.nchunk) Mg = fmaxf(Mg, pm[u]);
+    if (Mg == -INFINITY) continue;  // nothing visible yet
+    const float r = exp2f(M - Mg);  // 0 when M is -inf
+    L *= r;
+    acc *= r;
+    M = Mg;
+#pragma unroll
+    for (int u = 0; u < CG; ++u) {
+      if (c0 + u >= a.nchunk || pm[u] == -INFINITY) continue;
+      const float w = exp2f(pm[u] - M);
+      L += w * pl[u];
+      acc += w * po[u];
+    }
   }
   if (!on) return;
   const float v = acc / L;

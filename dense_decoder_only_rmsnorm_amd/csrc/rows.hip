@@ -63,9 +63,19 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(NormArgs a) {
     if (i < D) {
       float4 t = *reinterpret_cast<const float4 *>(x + i);
       if (a.nsplit > 0) {
-        for (int s = 0; s < a.nsplit; ++s) {
-          const float4 p = *reinterpret_cast<const float4 *>(a.part + s * a.part_stride + (int64_t)r * D + i);
-          t.x += p.x; t.y += p.y; t.z += p.z; t.w += p.w;
+        // partials in groups of 8: the group's loads (clamped to a valid
+        // plane, the extra ones weighted 0) are issued together instead of
+        // one latency per plane
+        for (int s0 = 0; s0 < a.nsplit; s0 += 8) {
+          float4 p[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            p[u] = *reinterpret_cast<const float4 *>(a.part + min(s0 + u, a.nsplit - 1) * a.part_stride + (int64_t)r * D + i);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float m = s0 + u < a.nsplit ? 1.f : 0.f;
+            t.x += m * p[u].x; t.y += m * p[u].y; t.z += m * p[u].z; t.w += m * p[u].w;
+          }
         }
         *reinterpret_cast<float4 *>(x + i) = t;
       }
@@ -160,10 +170,17 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(RopeQkvArgs a) {
   const int j = (int)(idx % npair) * 2;  // even column
   const int N = (a.H + 2 * a.G) * a.hd;
   float x0 = 0.f, x1 = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float2 t = *reinterpret_cast<const float2 *>(a.part + s * a.part_stride + (int64_t)r * N + j);
-    x0 += t.x;
-    x1 += t.y;
+  for (int s0 = 0; s0 < a.nsplit; s0 += 8) {  // loads of 8 partials at a time (see rmsnorm_kernel)
+    float2 t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      t[u] = *reinterpret_cast<const float2 *>(a.part + min(s0 + u, a.nsplit - 1) * a.part_stride + (int64_t)r * N + j);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float m = s0 + u < a.nsplit ? 1.f : 0.f;
+      x0 += m * t[u].x;
+      x1 += m * t[u].y;
+    }
   }
   const int b = r / a.S, sidx = r % a.S;
   int p0 = a.pos ? a.pos[b] : a.start_pos;
