@@ -46,7 +46,9 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// silu(x) = x / (1 + e^-x), the quotient through the hardware reciprocal
+// (about 1 ulp; the result is rounded to bf16 or compared at fp32 tolerance)
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // (a + i b) * (c + i s): the rotation of one RoPE pair by an angle with
 // cosine c and sine s.

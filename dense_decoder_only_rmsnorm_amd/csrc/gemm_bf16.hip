@@ -251,14 +251,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int CN = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
   constexpr int LDC = CN + 8;
   u16 *Cs = smem;  // [BM][LDC], reuses the operand buffers (loop ended with a barrier)
-  const int pbase = m0 % a.S;  // sequence position of tile row 0 (RoPE table row = row % S)
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    // QKV: table row offsets of this lane's 16 rows in row block i (shared by
-    // all its column blocks).  Rows past the matrix are clamped to its last
-    // row so every lookup stays inside the table; their values are not stored.
-    int toff[16];
-    if (EPI == EPI_QKV_ROPE) {
+  if (EPI == EPI_QKV_ROPE) {
+    // Table row offsets of this lane's 16 rows of row block i.  Rows past the
+    // matrix are clamped to its last row so every lookup stays inside the
+    // table; their values are not stored.
+    const int pbase = m0 % a.S;  // sequence position of tile row 0 (table row = row % S)
+    auto row_offsets = [&](int i, int *toff) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int x = min(rloc + i * 32 + 8 * (r / 4) + (r % 4), a.M - 1 - m0);
@@ -271,40 +269,75 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
           p %= a.S;
         toff[r] = p * (a.hd / 2);
       }
-    }
+    };
+    // A 32-column block lies inside one head of one of q, k, v (the head size
+    // is a multiple of 32, checked at launch), so whether it rotates and its
+    // table column are the same for the whole block.  v blocks read a valid
+    // table entry and apply the identity.
+    const int Hq = a.H * a.hd, Hk = a.G * a.hd;
+    int dh[FN];
+    bool rot[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      if (EPI == EPI_SWIGLU) {
-        if (j & 1) continue;  // the up block j+1 is consumed with its gate block j
-        const int ccol = (wn * WN / 64 + j / 2) * 32 + col_l;
+      const int col0 = n0 + wn * WN + j * 32;
+      rot[j] = col0 < Hq + Hk;
+      dh[j] = rot[j] ? (((col0 < Hq ? col0 : col0 - Hq) % a.hd) + col_l) >> 1 : 0;
+    }
+    // pair (2t, 2t+1) sits in lanes (2t, 2t+1) of one row:
+    //   even: x0 cos - x1 sin,  odd: x1 cos + x0 sin
+    const float sgn = (lane & 1) ? 1.f : -1.f;
+    // the table entries of block q+1 are loaded while block q is rotated
+    // (row offsets of row blocks i and i+1 live at a time)
+    constexpr int NQ = FM * FN;
+    int toff[2][16];
+    row_offsets(0, toff[0]);
+    float2 cs[2][16];
+    // (32-bit byte offsets from the table base: loads take a scalar base)
+    const char *tab = reinterpret_cast<const char *>(a.tab);
+    auto tab_at = [&](int e) { return *reinterpret_cast<const float2 *>(tab + (uint32_t)e * 8u); };
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cs[0][r] = tab_at(toff[0][r] + dh[0]);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int i = q / FN, j = q % FN;
+      if (j == 0 && i + 1 < FM) row_offsets(i + 1, toff[(i + 1) & 1]);
+      if (q + 1 < NQ) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cs[(q + 1) & 1][r] = tab_at(toff[((q + 1) / FN) & 1][r] + dh[(q + 1) % FN]);
+      }
+      const int ccol = wn * WN + j * 32 + col_l;
+      if (rot[j]) {  // wave-uniform
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int rr = rloc + i * 32 + 8 * (r / 4) + (r % 4);
-          Cs[rr * LDC + ccol] = f2bf(silu(acc[i][j][r]) * acc[i][j + 1][r]);
+          const float v = acc[i][j][r];
+          const float pv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+          Cs[rr * LDC + ccol] = f2bf(fmaf(pv, sgn * cs[q & 1][r].y, v * cs[q & 1][r].x));
         }
       } else {
-        const int ccol = wn * WN + j * 32 + col_l;
-        // A 32-column block lies inside one head of one of q, k, v (the head
-        // size is a multiple of 32, checked at launch), so whether it rotates
-        // and its first head dimension are the same for the whole wave.
-        const int col0 = n0 + wn * WN + j * 32;
-        const int Hq = a.H * a.hd, Hk = a.G * a.hd;
-        if (EPI == EPI_QKV_ROPE && col0 < Hq + Hk) {
-          const int dh = (((col0 < Hq ? col0 : col0 - Hq) % a.hd) + col_l) >> 1;  // table column
-          // pair (2t, 2t+1) sits in lanes (2t, 2t+1) of one row:
-          //   even: x0 cos - x1 sin,  odd: x1 cos + x0 sin
-          const float sgn = (lane & 1) ? 1.f : -1.f;
-          float2 cs[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) cs[r] = a.tab[toff[r] + dh];
+        for (int r = 0; r < 16; ++r) {
+          const int rr = rloc + i * 32 + 8 * (r / 4) + (r % 4);
+          Cs[rr * LDC + ccol] = f2bf(acc[i][j][r]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keeps the loads one block ahead, not all hoisted
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if (EPI == EPI_SWIGLU) {
+          if (j & 1) continue;  // the up block j+1 is consumed with its gate block j
+          const int ccol = (wn * WN / 64 + j / 2) * 32 + col_l;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rr = rloc + i * 32 + 8 * (r / 4) + (r % 4);
-            const float v = acc[i][j][r];
-            const float pv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-            Cs[rr * LDC + ccol] = f2bf(fmaf(pv, sgn * cs[r].y, v * cs[r].x));
+            Cs[rr * LDC + ccol] = f2bf(silu(acc[i][j][r]) * acc[i][j + 1][r]);
           }
         } else {
+          const int ccol = wn * WN + j * 32 + col_l;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rr = rloc + i * 32 + 8 * (r / 4) + (r % 4);
@@ -312,7 +345,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
           }
         }
       }
-    }
   }
   __syncthreads();
   constexpr int CPR = CN / 8;  // 16-byte pieces per tile row
