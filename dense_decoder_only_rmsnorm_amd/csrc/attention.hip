@@ -184,14 +184,17 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(AttnArgs a) {
 //
 // A block covers 256 query rows of one KV group g: the group's n_rep heads
 // times 256/n_rep positions, so each K/V tile in LDS serves every head of
-// the group [P2 3.4 repeat_kv; P1 8].  Wave w owns rows 64w .. 64w+63 as two
-// 32-row blocks.  Per 64-key tile:
+// the group [P2 3.4 repeat_kv; P1 8].  Each of the eight waves owns 32 query
+// rows with its Q fragments in registers.  Per 64-key tile:
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16; A = K rows from LDS, B = Q
 //                    fragments kept in registers.  Lane l holds the scores of
 //                    query l%32 for keys 8*(r/4) + 4*(l/32) + r%4.
 //   online softmax   in fp32, log2 units, per query in its own lane.
 //   O^T += V^T P^T   A = V^T read from row-major V with ds_read_b64_tr_b16,
 //                    B = P^T taken from the score registers as bf16.
+// Two waves share each SIMD, so one wave's softmax (vector ALU, exp) runs
+// while the other's MFMAs do, and each fills the other's gaps between
+// dependent MFMAs (S^T has only two accumulator blocks per wave).
 // K and V arrive with global_load_lds_dwordx4 (no VGPR round trip) while the
 // previous tile is being computed.  Rows are 256 bytes; K and Q keep 16-byte
 // chunk c of row r at c ^ (r & 15), so the 32 rows a fragment read touches
@@ -199,277 +202,6 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(AttnArgs a) {
 // Block order: consecutive block ids cycle through the KV groups, so the
 // blocks one XCD receives (ids congruent mod 8) share a group's K/V in L2;
 // within a group the longest causal ranges start first.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attn_fwd_tiled128(AttnArgs a) {
-  constexpr int HD = 128;
-  constexpr int KT = 64;            // keys per tile
-  constexpr int TILE = KT * HD;     // elements per K or V tile
-  constexpr int NT = HD / 16;       // S^T k-steps over head_dim
-  constexpr int NO = HD / 32;       // O^T row blocks over head_dim
-  __shared__ __align__(16) u16 Ks[2][TILE];
-  __shared__ __align__(16) u16 Vs[2][TILE];
-  __shared__ __align__(16) u16 Qs[256 * HD];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_rep = a.H / a.G;
-  const int QB = 256 / n_rep;  // positions per block
-  const int nq = (a.S + QB - 1) / QB;
-  const int L = blockIdx.x;
-  const int g = L % a.G;
-  const int rest = L / a.G;
-  const int b = rest % a.B;
-  const int qblk = nq - 1 - rest / a.B;
-
-  const int hf = lane >> 5;  // half of the wave
-  const u16 *Q = static_cast<const u16 *>(a.q);
-  int qpos[2];
-  bool valid[2];
-  int hq[2], srow[2];
-  int wmax = 0, wmin = INT32_MAX;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int rho = wave * 64 + qb * 32 + (lane & 31);
-    hq[qb] = g * n_rep + rho / QB;
-    const int sq = qblk * QB + rho % QB;
-    valid[qb] = sq < a.S;
-    srow[qb] = valid[qb] ? sq : a.S - 1;
-    qpos[qb] = a.start_pos + srow[qb];
-    wmax = max(wmax, qpos[qb]);
-    wmin = min(wmin, qpos[qb]);
-  }
-  wmax = (int)wave_max((float)wmax);
-  wmin = -(int)wave_max((float)-wmin);
-  // Q rows of this block -> LDS (row rho = 64*wave + 32*qb + i; same chunk
-  // swizzle as K).  Wave w stages its own 64 rows: 16 pieces of 4 rows.
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int rho = wave * 64 + 4 * i + (lane >> 4);
-    const int sq = min(qblk * QB + rho % QB, a.S - 1);
-    const int hh = g * n_rep + rho / QB;
-    const int cc = ((lane & 15) ^ (rho & 15)) * 8;
-    __builtin_amdgcn_global_load_lds((const void *)(Q + (int64_t)(b * a.S + sq) * a.q_stride + hh * HD + cc),
-                                     (__attribute__((address_space(3))) void *)(Qs + (wave * 64 + 4 * i) * HD), 16,
-                                     0, 0);
-  }
-
-  const int last_s = min(a.S, (qblk + 1) * QB) - 1;
-  const int kv_end = a.start_pos + last_s + 1;  // keys [0, kv_end)
-  const int ntiles = (kv_end + KT - 1) / KT;
-  const int64_t kstride = (int64_t)a.G * HD;
-  const u16 *Kg = static_cast<const u16 *>(a.k) + ((int64_t)b * a.kcap * a.G + g) * HD;
-  const u16 *Vg = static_cast<const u16 *>(a.v) + ((int64_t)b * a.kcap * a.G + g) * HD;
-
-  // loader: piece p = wave + 4i (i < 4) covers tile rows 4p .. 4p+3; lane L
-  // -> row 4p + L/16, physical chunk L%16 holding logical chunk (L%16)^(row&15)
-  // V rows use a second swizzle, vswz(r) = ((r & 3) << 2) | ((r >> 2) & 3):
-  // a transposed read touches 4 consecutive rows x 4 chunks, and this spreads
-  // them over all 16 chunk positions (r & 15 would keep them in one group of
-  // four and serialise the read 4 ways).
-  int lrow[4], lcol[4], lcolv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = wave + 4 * i;
-    lrow[i] = 4 * p + (lane >> 4);
-    lcol[i] = ((lane & 15) ^ (lrow[i] & 15)) * 8;
-    lcolv[i] = ((lane & 15) ^ (((lrow[i] & 3) << 2) | ((lrow[i] >> 2) & 3))) * 8;
-  }
-  auto issue = [&](int kt, int buf) {
-    const int k0 = kt * KT;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(k0 + lrow[i], kv_end - 1);  // rows past the end are masked
-      const int p = __builtin_amdgcn_readfirstlane(wave + 4 * i);
-      __builtin_amdgcn_global_load_lds((const void *)(Kg + (int64_t)key * kstride + lcol[i]),
-                                       (__attribute__((address_space(3))) void *)(Ks[buf] + p * 4 * HD), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(Vg + (int64_t)key * kstride + lcolv[i]),
-                                       (__attribute__((address_space(3))) void *)(Vs[buf] + p * 4 * HD), 16, 0, 0);
-    }
-  };
-
-  f32x16 o[2][NO];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int i = 0; i < NO; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[qb][i][r] = 0.f;
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  const float c = a.scale * kLog2e;
-
-  // V^T fragment addressing (tr16 reads): 16-lane group G = lane/16 reads rows
-  // 4*hf + j/4 (+8 for the second half) of a 16-key step, columns
-  // 32*ob + 16*(G&1) + 4*(j&3) .. +3; lane j then holds V[4 keys][d], d = 32*ob + lane%32.
-  const int jj = lane & 15, dg = (lane >> 4) & 1;
-  const int vr0 = 4 * hf + (jj >> 2);
-  const int vq = 2 * dg + ((jj & 3) >> 1), vhalf = (jj & 1) * 4;
-
-  // one 64-key tile: MASK is true only for tiles that reach past the
-  // wave's smallest query position
-  auto tile = [&](int kt, auto mask_c) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    const int k0 = kt * KT;
-    const u16 *ks = Ks[kt & 1];
-    const u16 *vs = Vs[kt & 1];
-
-    // S^T = K Q^T: two 32-key blocks x two 32-query blocks.  Rows kb*32 + i
-    // of K and 64*wave + 32*qb + i of Q (i = lane % 32) share the swizzle
-    // i & 15; the fragments of head-dim step t+1 are read while the four
-    // MFMAs of step t run.
-    f32x16 sc[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kb][qb][r] = 0.f;
-    const u16 *krow = ks + (lane & 31) * HD;
-    const u16 *qrow = Qs + (wave * 64 + (lane & 31)) * HD;
-    const int isw = lane & 15;
-    bf16x8 kf[2][2], qf[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      kf[0][x] = *reinterpret_cast<const bf16x8 *>(krow + x * 32 * HD + ((hf ^ isw) * 8));
-      qf[0][x] = *reinterpret_cast<const bf16x8 *>(qrow + x * 32 * HD + ((hf ^ isw) * 8));
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int cb = t & 1;
-      if (t + 1 < NT) {
-        const int co = ((2 * (t + 1) + hf) ^ isw) * 8;
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          kf[cb ^ 1][x] = *reinterpret_cast<const bf16x8 *>(krow + x * 32 * HD + co);
-          qf[cb ^ 1][x] = *reinterpret_cast<const bf16x8 *>(qrow + x * 32 * HD + co);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cb][kb], qf[cb][qb], sc[kb][qb], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // online softmax per query, in log2 units.  The running maximum m only
-    // moves when a tile's maximum exceeds it by more than 8 (P then stays
-    // below 2^8 and the sum l uses the same m, so the result is exact); the
-    // rescale of O is therefore rare and wave-uniform.
-    float tmax[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (MASK) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key > qpos[qb]) sc[kb][qb][r] = -INFINITY;
-          }
-          mx = fmaxf(mx, sc[kb][qb][r]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      tmax[qb] = mx * c;  // c > 0: the maximum commutes with the scale
-    }
-    const bool grow = (tmax[0] > m[0] + 8.f) || (tmax[1] > m[1] + 8.f);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float m_new = fmaxf(m[qb], tmax[qb]);  // finite: key 0 is visible to every query
-        const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_new);
-        l[qb] *= alpha;
-        m[qb] = m_new;
-#pragma unroll
-        for (int i = 0; i < NO; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[qb][i][r] *= alpha;
-      }
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][r], c, -m[qb]));
-          sc[kb][qb][r] = p;
-          rs += p;
-        }
-      rs += __shfl_xor(rs, 32, kWave);
-      l[qb] += rs;
-    }
-    // O^T += V^T P^T over four 16-key steps
-#pragma unroll
-    for (int ksp = 0; ksp < 4; ++ksp) {
-      const int kb = ksp >> 1, t = ksp & 1;
-      bf16x8 pf[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[qb][e] = (__bf16)sc[kb][qb][8 * t + e];
-      const int rbase = 16 * ksp + vr0;
-#pragma unroll
-      for (int ob = 0; ob < NO; ++ob) {
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        u32x2 wv[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int r = rbase + 8 * h2;
-          const int vsw = ((r & 3) << 2) | ((r >> 2) & 3);
-          const int off = (r * HD + (((4 * ob + vq) ^ vsw) * 8) + vhalf) * (int)sizeof(u16);
-          const v4s w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s *)((__attribute__((address_space(3))) const char *)vs + off));
-          wv[h2] = __builtin_bit_cast(u32x2, w);
-        }
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(wv[0].x, wv[0].y, wv[1].x, wv[1].y));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          o[qb][ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], o[qb][ob], 0, 0, 0);
-      }
-    }
-  };
-
-  // tiles [0, nfull) are visible to every query of this wave; the rest are
-  // masked, and tiles past the wave's last query are skipped.  Every wave
-  // passes the same ntiles barriers.
-  const int nfull = min(ntiles, (wmin + 1) / KT);
-  issue(0, 0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();  // tile kt has landed; every wave is done with tile kt-1
-    if (kt + 1 < ntiles) issue(kt + 1, (kt + 1) & 1);
-    if (kt < nfull)
-      tile(kt, std::integral_constant<bool, false>());
-    else if (kt * KT <= wmax)
-      tile(kt, std::integral_constant<bool, true>());
-  }
-
-  // lane holds O^T[d = 32*ob + 8*(r/4) + 4*hf + r%4][query lane%32]
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    if (!valid[qb]) continue;
-    const float inv = 1.0f / l[qb];
-    u16 *orow = static_cast<u16 *>(a.o) + (int64_t)(b * a.S + srow[qb]) * a.q_stride + hq[qb] * HD;
-#pragma unroll
-    for (int ob = 0; ob < NO; ++ob)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = ob * 32 + 8 * q4 + 4 * hf;
-        uint2 pk;
-        pk.x = (uint32_t)f2bf(o[qb][ob][q4 * 4 + 0] * inv) | ((uint32_t)f2bf(o[qb][ob][q4 * 4 + 1] * inv) << 16);
-        pk.y = (uint32_t)f2bf(o[qb][ob][q4 * 4 + 2] * inv) | ((uint32_t)f2bf(o[qb][ob][q4 * 4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2 *>(orow + d) = pk;
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Prefill, bf16, head_dim 128, eight waves: the same block of 256 query rows
-// of one KV group and the same K/V tile pipeline as attn_fwd_tiled128, but
-// each wave owns 32 query rows with its Q fragments in registers.  Two waves
-// share each SIMD, so one wave's softmax (vector ALU, exp) runs while the
-// other's MFMAs do, instead of one wave alternating between them.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
   constexpr int HD = 128;
@@ -1258,11 +990,7 @@ hipError_t prefill_hd(int dtype, const AttnArgs &a, hipStream_t s) {
   if (dtype == 1 && HD == 128) {
     const int QB = 256 / (a.H / a.G);
     const int nblk = ((a.S + QB - 1) / QB) * a.G * a.B;
-#ifdef ATTN_TILED4
-    hipLaunchKernelGGL(attn_fwd_tiled128, dim3(nblk), dim3(256), 0, s, a);
-#else
     hipLaunchKernelGGL(attn_fwd_w8, dim3(nblk), dim3(512), 0, s, a);
-#endif
   } else if (dtype == 1) {
     const int QB = 128 / (a.H / a.G);
     dim3 grid((a.S + QB - 1) / QB, a.G, a.B);
