@@ -5,8 +5,9 @@ kernels of ``libllama_mi355x.so`` (built from ``csrc/`` by ``build.py``),
 called through its C ABI (``include/llama_mi355x.h``).  PyTorch supplies
 device memory and streams.  The entry points keep the C names:
 ``llama_layer_forward``, ``llama_prefill``, ``llama_decode_step``,
-``lm_head_argmax``, plus ``llama_ffn_hidden_dim`` and
-``llama_workspace_bytes``.
+``lm_head_argmax``, ``llama_sample_top_p``, ``llama_generate``, plus
+``llama_ffn_hidden_dim``, ``llama_workspace_bytes`` and
+``llama_generate_workspace_bytes``.
 
 Loading fails loudly when the library has not been built: there is no
 fallback implementation.
@@ -25,7 +26,9 @@ LLAMA_F32, LLAMA_BF16 = 0, 1
 ERROR_NAMES = {-1: "LLAMA_ERR_ARG", -2: "LLAMA_ERR_SHAPE", -3: "LLAMA_ERR_UNSUPPORTED", -4: "LLAMA_ERR_WORKSPACE",
                -5: "LLAMA_ERR_HIP"}
 EXPORTED = ("llama_ffn_hidden_dim", "llama_workspace_bytes", "llama_layer_forward", "llama_prefill",
-            "llama_decode_step", "lm_head_argmax", "llama_last_error", "llama_timing_enable", "llama_timing_report")
+            "llama_decode_step", "lm_head_argmax", "llama_sample_top_p", "llama_generate_workspace_bytes",
+            "llama_generate", "llama_last_error", "llama_timing_enable", "llama_timing_report")
+LLAMA_GEN_NO_GRAPH = 1
 
 
 class LlamaError(RuntimeError):
@@ -84,6 +87,14 @@ def lib() -> ctypes.CDLL:
         L.llama_decode_step.restype = ctypes.c_int
         L.lm_head_argmax.argtypes = [A, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         L.lm_head_argmax.restype = ctypes.c_int
+        L.llama_sample_top_p.argtypes = [vp, i32, i32, ctypes.c_float, ctypes.c_float, vp, vp, vp]
+        L.llama_sample_top_p.restype = ctypes.c_int
+        L.llama_generate_workspace_bytes.argtypes = [A, i32, i32]
+        L.llama_generate_workspace_bytes.restype = sz
+        L.llama_generate.argtypes = [A, ctypes.POINTER(llama_model_w), vp, i32, ctypes.POINTER(i32), i32, i32, i32,
+                                     ctypes.c_float, ctypes.c_float, vp, ctypes.POINTER(llama_kv), vp, vp, i32,
+                                     ctypes.POINTER(i32), vp, sz, vp]
+        L.llama_generate.restype = ctypes.c_int
         L.llama_timing_enable.argtypes = [ctypes.c_int]
         L.llama_timing_enable.restype = ctypes.c_int
         L.llama_timing_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
@@ -191,6 +202,32 @@ def lm_head_argmax(args: llama_args, h, final_norm_w, w_out, M: int, logits=None
     _check(rc)
 
 
+def llama_sample_top_p(logits, M: int, V: int, temperature: float, top_p: float, u, out_id, stream=None):
+    rc = lib().llama_sample_top_p(_p(logits), M, V, temperature, top_p, _p(u), _p(out_id), _stream(stream))
+    _check(rc)
+
+
+def llama_generate_workspace_bytes(args: llama_args, batch: int, max_prompt_len: int) -> int:
+    n = lib().llama_generate_workspace_bytes(ctypes.byref(args), batch, max_prompt_len)
+    if n == 0:
+        raise LlamaError(LLAMA_ERR_ARG, last_error() or "invalid arguments")
+    return n
+
+
+def llama_generate(args: llama_args, model, prompt, prompt_stride: int, prompt_len: Sequence[int], batch: int,
+                   max_gen_len: int, eos_id: int, temperature: float, top_p: float, uniforms, kv, tokens, out_len,
+                   flags: int = 0, ws=None, stream=None) -> int:
+    """``prompt_len`` is a host sequence; returns the number of decode steps run."""
+    m = model[0]
+    lens = (ctypes.c_int32 * max(1, len(prompt_len)))(*[int(x) for x in prompt_len])
+    steps = ctypes.c_int32(0)
+    rc = lib().llama_generate(ctypes.byref(args), ctypes.byref(m), _p(prompt), prompt_stride, lens, batch,
+                              max_gen_len, eos_id, temperature, top_p, _p(uniforms), kv, _p(tokens), _p(out_len),
+                              flags, ctypes.byref(steps), _p(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc)
+    return steps.value
+
+
 def llama_timing_enable(on: bool = True):
     _check(lib().llama_timing_enable(1 if on else 0))
 
@@ -210,4 +247,5 @@ def llama_timing_report() -> dict:
 __all__ = ["llama_timing_enable", "llama_timing_report", "lib", "last_error", "LlamaError", "llama_args", "llama_layer_w", "llama_model_w", "llama_kv",
            "make_args", "layer_struct", "model_struct", "kv_array", "llama_ffn_hidden_dim",
            "llama_workspace_bytes", "llama_layer_forward", "llama_prefill", "llama_decode_step", "lm_head_argmax",
+           "llama_sample_top_p", "llama_generate_workspace_bytes", "llama_generate", "LLAMA_GEN_NO_GRAPH",
            "LLAMA_F32", "LLAMA_BF16", "EXPORTED"]

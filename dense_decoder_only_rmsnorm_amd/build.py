@@ -18,7 +18,7 @@ OUT = os.path.join(HERE, "libllama_mi355x.so")
 OBJDIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "rows.hip", "gemm_bf16.hip", "skinny.hip", "attention.hip"]
+SOURCES = ["api.hip", "rows.hip", "gemm_bf16.hip", "skinny.hip", "attention.hip", "generate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

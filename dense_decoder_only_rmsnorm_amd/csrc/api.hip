@@ -505,6 +505,51 @@ int check_layer_w(const llama_layer_w *lw) {
   return LLAMA_OK;
 }
 
+// ------------------------------- generation layout ---------------------------
+constexpr int64_t kGenPrefillTokens = 16384;  // tokens per prefill call inside generation
+constexpr int kGenCheckEvery = 8;             // decode steps between early-stop checks
+constexpr int kSampleMaxVocab = 131072;       // 1024 threads x 128 ids per sampler block
+
+struct GenWs {
+  GenState st;
+  float *logits;   // [B][V] fp32 (sampling)
+  int32_t *ids;    // staged prompt rows of one prefill call
+  void *rest;      // prefill / decode workspace
+  size_t rest_bytes;
+};
+
+int gen_rows_per_call(int L, int B) {
+  return (int)std::max<int64_t>(1, std::min<int64_t>(B, kGenPrefillTokens / L));
+}
+
+// Largest prefill or decode workspace any call inside generation can need.
+size_t gen_inner_bytes(const Dims &d, int B, int Lmax, int cap) {
+  size_t need = decode_bytes(d, B, cap);
+  for (int g = 1; g <= B; ++g) {
+    // the longest prompt length prefilled g at a time
+    const int64_t L = g == 1 ? Lmax : std::min<int64_t>(Lmax, kGenPrefillTokens / g);
+    if (L < 1) break;
+    need = std::max(need, prefill_bytes(d, gen_rows_per_call((int)L, B), (int)L));
+  }
+  return need;
+}
+
+GenWs carve_gen(Carver &c, const Dims &d, int B, int Lmax, int cap) {
+  GenWs w{};
+  w.st.cur = c.take<int32_t>(B);
+  w.st.pos = c.take<int32_t>(B);
+  w.st.done = c.take<int32_t>(B);
+  w.st.end = c.take<int32_t>(B);
+  w.st.next = c.take<int32_t>(B);
+  w.st.gidx = c.take<int32_t>(B);
+  w.st.active = c.take<int32_t>(1);
+  w.logits = c.take<float>((size_t)B * d.V);
+  w.ids = c.take<int32_t>((size_t)B * Lmax);
+  w.rest_bytes = gen_inner_bytes(d, B, Lmax, cap);
+  w.rest = c.take<char>(w.rest_bytes);
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -810,6 +855,173 @@ int lm_head_argmax(const llama_args *a, const float *h, const void *final_norm_w
       return e;
   }
   return run_head(d, hw, w_out, M, logits, argmax, s);
+}
+
+int llama_sample_top_p(const float *logits, int32_t M, int32_t V, float temperature, float top_p, const float *u,
+                       int32_t *out_id, void *stream) {
+  if (!logits || !u || !out_id) return fail(LLAMA_ERR_ARG, "logits, u or out_id is NULL");
+  if (M < 1 || V < 1) return fail(LLAMA_ERR_ARG, "M and V must be >= 1");
+  if (!(temperature > 0.f)) return fail(LLAMA_ERR_ARG, "temperature must be > 0");
+  if (!(top_p >= 0.f)) return fail(LLAMA_ERR_ARG, "top_p must be >= 0");
+  if (V > kSampleMaxVocab) return fail(LLAMA_ERR_UNSUPPORTED, "vocab %d above %d", V, kSampleMaxVocab);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LAUNCH("sample_top_p", launch_sample_top_p(logits, V, M, V, temperature, top_p, u, 1, nullptr, out_id, s));
+  return LLAMA_OK;
+}
+
+size_t llama_generate_workspace_bytes(const llama_args *a, int32_t batch, int32_t max_prompt_len) {
+  Dims d;
+  if (check_model(a, d) != LLAMA_OK || batch < 1 || batch > kGenMaxBatch || max_prompt_len < 1 ||
+      a->max_seq_len < 1)
+    return 0;
+  Carver c(nullptr);
+  carve_gen(c, d, batch, max_prompt_len, a->max_seq_len);
+  return c.off + 256;
+}
+
+int llama_generate(const llama_args *a, const llama_model_w *w, const int32_t *prompt, int32_t prompt_stride,
+                   const int32_t *prompt_len, int32_t batch, int32_t max_gen_len, int32_t eos_id, float temperature,
+                   float top_p, const float *uniforms, const llama_kv *kv, int32_t *tokens, int32_t *out_len,
+                   int32_t flags, int32_t *steps_run, void *ws, size_t ws_bytes, void *stream) {
+  Dims d;
+  if (int e = check_model(a, d)) return e;
+  if (!w || !w->tok_embeddings || !w->norm || !w->output || (d.L > 0 && !w->layers))
+    return fail(LLAMA_ERR_ARG, "model weight pointer is NULL");
+  for (int l = 0; l < d.L; ++l)
+    if (int e = check_layer_w(&w->layers[l])) return e;
+  if (!prompt || !prompt_len || !tokens || !out_len || !ws || (d.L > 0 && !kv))
+    return fail(LLAMA_ERR_ARG, "prompt, prompt_len, kv, tokens, out_len or ws is NULL");
+  for (int l = 0; l < d.L; ++l)
+    if (!kv[l].k || !kv[l].v) return fail(LLAMA_ERR_ARG, "kv[%d] has a NULL pointer", l);
+  if (batch < 1) return fail(LLAMA_ERR_ARG, "batch must be >= 1");
+  if (batch > kGenMaxBatch) return fail(LLAMA_ERR_UNSUPPORTED, "generation batch %d above %d", batch, kGenMaxBatch);
+  if (batch > a->max_batch_size) return fail(LLAMA_ERR_SHAPE, "batch %d > max_batch_size %d", batch, a->max_batch_size);
+  if (max_gen_len < 0) return fail(LLAMA_ERR_ARG, "max_gen_len < 0");
+  if (!(temperature >= 0.f)) return fail(LLAMA_ERR_ARG, "temperature must be >= 0");
+  const bool samp = temperature > 0.f;
+  if (samp) {
+    if (!uniforms) return fail(LLAMA_ERR_ARG, "sampling needs uniforms");
+    if (!(top_p >= 0.f)) return fail(LLAMA_ERR_ARG, "top_p must be >= 0");
+    if (d.V > kSampleMaxVocab) return fail(LLAMA_ERR_UNSUPPORTED, "vocab %d above %d", d.V, kSampleMaxVocab);
+  }
+  const int cap = a->max_seq_len;
+  if (cap < 1) return fail(LLAMA_ERR_SHAPE, "max_seq_len < 1");
+  GenLens lens{};
+  int Lmax = 0, steps = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int L = prompt_len[b];
+    if (L < 1 || L > cap) return fail(LLAMA_ERR_ARG, "prompt_len[%d] = %d outside [1, %d]", b, L, cap);
+    lens.L[b] = L;
+    lens.total[b] = (int32_t)std::min<int64_t>((int64_t)L + max_gen_len, cap);
+    Lmax = std::max(Lmax, L);
+    steps = std::max(steps, lens.total[b] - L - 1);  // decode steps after the prefill's choice
+  }
+  if (prompt_stride < Lmax) return fail(LLAMA_ERR_ARG, "prompt_stride %d < longest prompt %d", prompt_stride, Lmax);
+  Carver probe(nullptr);
+  carve_gen(probe, d, batch, Lmax, cap);
+  if (ws_bytes < probe.off) return fail(LLAMA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, probe.off);
+  if ((uintptr_t)ws % 256) return fail(LLAMA_ERR_ARG, "workspace not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  GenWs gw = carve_gen(c, d, batch, Lmax, cap);
+  const int B = batch;
+  bool any = false;
+  for (int b = 0; b < B; ++b) any |= lens.total[b] > lens.L[b];
+
+  LAUNCH("gen_fill", launch_gen_fill(prompt, prompt_stride, tokens, cap, lens, B, s));
+  int32_t ran = 0;
+  if (any) {
+    // prompts: consecutive sequences of equal length share a prefill call
+    std::vector<llama_kv> kvg(std::max(d.L, 1));
+    for (int b0 = 0; b0 < B;) {
+      const int L = lens.L[b0];
+      const int gmax = gen_rows_per_call(L, B);
+      int b1 = b0 + 1;
+      while (b1 < B && lens.L[b1] == L && b1 - b0 < gmax) ++b1;
+      const int g = b1 - b0;
+      HIPCHK(hipMemcpy2DAsync(gw.ids, (size_t)L * 4, prompt + (int64_t)b0 * prompt_stride, (size_t)prompt_stride * 4,
+                              (size_t)L * 4, g, hipMemcpyDeviceToDevice, s));
+      const size_t row_bytes = (size_t)cap * d.Hk() * d.esz;
+      for (int l = 0; l < d.L; ++l) {
+        kvg[l].k = static_cast<char *>(kv[l].k) + (size_t)b0 * row_bytes;
+        kvg[l].v = static_cast<char *>(kv[l].v) + (size_t)b0 * row_bytes;
+      }
+      if (int e = llama_prefill(a, w, gw.ids, g, L, d.L > 0 ? kvg.data() : nullptr, nullptr,
+                                samp ? gw.logits + (int64_t)b0 * d.V : nullptr, gw.st.next + b0, gw.rest,
+                                gw.rest_bytes, stream))
+        return e;
+      b0 = b1;
+    }
+    if (samp)
+      LAUNCH("sample_top_p", launch_sample_top_p(gw.logits, d.V, B, d.V, temperature, top_p, uniforms,
+                                                 std::max(max_gen_len, 1), nullptr, gw.st.next, s));
+  }
+  // the prefill's choice becomes each sequence's first generated token (a
+  // sequence with nothing to generate parks on its last prompt position)
+  LAUNCH("gen_step", launch_gen_step(gw.st, lens, B, eos_id, prompt, prompt_stride, tokens, cap, 1, s));
+  if (any) {
+    // one step: decode at each sequence's position, choose, append
+    auto one_step = [&]() -> int {
+      if (int e = llama_decode_step(a, w, gw.st.cur, gw.st.pos, B, kv, samp ? gw.logits : nullptr, gw.st.next,
+                                    gw.rest, gw.rest_bytes, stream))
+        return e;
+      if (samp)
+        LAUNCH("sample_top_p", launch_sample_top_p(gw.logits, d.V, B, d.V, temperature, top_p, uniforms,
+                                                   std::max(max_gen_len, 1), gw.st.gidx, gw.st.next, s));
+      LAUNCH("gen_step", launch_gen_step(gw.st, lens, B, eos_id, prompt, prompt_stride, tokens, cap, 0, s));
+      return LLAMA_OK;
+    };
+    bool timing_on;
+    {
+      std::lock_guard<std::mutex> lk(g_timing.mu);
+      timing_on = g_timing.on;
+    }
+    const bool use_graph = steps > 0 && !(flags & LLAMA_GEN_NO_GRAPH) && s != nullptr && !timing_on;
+    hipGraphExec_t ge = nullptr;
+    if (use_graph) {
+      HIPCHK(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+      const int e = one_step();
+      hipGraph_t graph = nullptr;
+      const hipError_t ec = hipStreamEndCapture(s, &graph);
+      if (e) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return e;
+      }
+      if (ec != hipSuccess) return fail(LLAMA_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(ec));
+      const hipError_t ei = hipGraphInstantiate(&ge, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      if (ei != hipSuccess) return fail(LLAMA_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(ei));
+    }
+    int rc = LLAMA_OK;
+    int32_t active = 1;
+    for (int t = 0; t < steps && rc == LLAMA_OK; ++t) {
+      if (t % kGenCheckEvery == 0) {
+        hipError_t e1 = hipMemcpyAsync(&active, gw.st.active, sizeof active, hipMemcpyDeviceToHost, s);
+        if (e1 == hipSuccess) e1 = hipStreamSynchronize(s);
+        if (e1 != hipSuccess) {
+          rc = fail(LLAMA_ERR_HIP, "reading the active count: %s", hipGetErrorString(e1));
+          break;
+        }
+        if (!active) break;
+      }
+      if (ge) {
+        const hipError_t e2 = hipGraphLaunch(ge, s);
+        if (e2 != hipSuccess) rc = fail(LLAMA_ERR_HIP, "hipGraphLaunch: %s", hipGetErrorString(e2));
+      } else {
+        rc = one_step();
+      }
+      if (rc == LLAMA_OK) ++ran;
+    }
+    if (ge) {
+      const hipError_t e3 = hipStreamSynchronize(s);
+      (void)hipGraphExecDestroy(ge);
+      if (rc == LLAMA_OK && e3 != hipSuccess) rc = fail(LLAMA_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e3));
+    }
+    if (rc) return rc;
+  }
+  LAUNCH("gen_finish", launch_gen_finish(gw.st, B, eos_id, tokens, cap, out_len, s));
+  if (steps_run) *steps_run = ran;
+  return LLAMA_OK;
 }
 
 const char *llama_last_error(void) { return g_err.c_str(); }

@@ -1,0 +1,340 @@
+// Token-generation loop state and the temperature / top-p sampler.
+//
+// Generation (P2 "Inference" section, the generate loop): after each
+// sequence's prompt, every step appends the model's choice for the next
+// position until the sequence has produced its end-of-text token or reached
+// its total length min(prompt + max_gen, max_seq_len).  The per-sequence
+// state lives in device memory so that a whole step (decode + this update)
+// can be replayed as one captured graph without host round trips.
+//
+// Sampling (P2 "Inference", sample_top_p; P3 temperature softmax): the
+// probabilities softmax(logits / T) are cut to the nucleus (the longest
+// prefix of the descending-probability order whose mass before each member
+// is at most top_p, ties ordered by token id), renormalised, and one token is
+// drawn with a caller-supplied uniform u in [0, 1) by inverse CDF over the
+// kept tokens in token-id order.
+//
+// Exactness of the sampler's decisions: each probability is carried as the
+// fixed-point integer q_i = floor(2^40 * z_i), z_i = 2^((l_i - max) * log2e / T)
+// in fp32.  Every sum (total, nucleus mass, prefix mass) is an exact u64 sum,
+// so the nucleus cut and the draw are independent of summation order: the
+// kernel's choice is a deterministic function of the logits, T, top_p and u.
+// The nucleus threshold is found by a 4-pass radix select (8 bits per pass)
+// over the fp32 bit pattern of z (monotone for z >= 0), with mass-weighted
+// histograms.
+#include "common.h"
+#include "kernels.h"
+
+namespace llk {
+
+// ---------------------------------------------------------------------------
+// generation state
+// ---------------------------------------------------------------------------
+// tokens[b][j] = prompt[b][j] for j < L[b], -1 after.  Grid (ceil(tstride/256), B).
+__global__ __launch_bounds__(256) void gen_fill_kernel(const int32_t *__restrict__ prompt, int64_t pstride,
+                                                       int32_t *__restrict__ tokens, int64_t tstride, GenLens lens) {
+  const int b = blockIdx.y;
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= tstride) return;
+  tokens[(int64_t)b * tstride + j] = j < lens.L[b] ? prompt[(int64_t)b * pstride + j] : -1;
+}
+
+// One block of 64 threads (B <= 64).  first = 1: take the prefill's choice
+// (next[b]) as the token at position L[b]; first = 0: append next[b] at
+// pos[b] + 1 for sequences still running.  Afterwards cur/pos hold the token
+// and position the next decode step feeds, gidx the index (0-based, counted
+// from the first generated token) of the token that step will produce, and
+// active[0] the number of running sequences.
+__global__ __launch_bounds__(64) void gen_step_kernel(GenState st, GenLens lens, int B, int eos,
+                                                      const int32_t *__restrict__ prompt, int64_t pstride,
+                                                      int32_t *__restrict__ tokens, int64_t tstride, int first) {
+  const int b = threadIdx.x;
+  int running = 0;
+  if (b < B) {
+    const int L = lens.L[b], tot = lens.total[b];
+    if (first) {
+      if (L >= tot) {
+        // nothing to generate: park on the prompt's last position (the decode
+        // steps of other sequences recompute it without effect on the output)
+        st.done[b] = 1;
+        st.pos[b] = L - 1;
+        st.cur[b] = prompt[(int64_t)b * pstride + L - 1];
+        st.end[b] = L;
+        st.gidx[b] = 0;
+      } else {
+        const int tok = st.next[b];
+        tokens[(int64_t)b * tstride + L] = tok;
+        st.end[b] = L + 1;
+        st.done[b] = (eos >= 0 && tok == eos) || L + 1 >= tot;
+        st.cur[b] = tok;
+        st.pos[b] = L;
+        st.gidx[b] = 1;
+      }
+    } else if (!st.done[b]) {
+      const int p = st.pos[b] + 1;
+      const int tok = st.next[b];
+      tokens[(int64_t)b * tstride + p] = tok;
+      st.end[b] = p + 1;
+      st.done[b] = (eos >= 0 && tok == eos) || p + 1 >= tot;
+      st.cur[b] = tok;
+      st.pos[b] = p;
+      st.gidx[b] = p + 1 - L;
+    }
+    running = !st.done[b];
+  }
+  const uint64_t m = __ballot(running);
+  if (b == 0) st.active[0] = __popcll(m);
+}
+
+// out_len[b] = index of the first end-of-text token in tokens[b][0, end[b]),
+// else end[b] (the output is cut at the first end-of-text token).  Grid B.
+__global__ __launch_bounds__(256) void gen_finish_kernel(GenState st, int eos, const int32_t *__restrict__ tokens,
+                                                         int64_t tstride, int32_t *__restrict__ out_len) {
+  const int b = blockIdx.x;
+  const int end = st.end[b];
+  int first = end;
+  if (eos >= 0)
+    for (int j = threadIdx.x; j < end; j += 256)
+      if (tokens[(int64_t)b * tstride + j] == eos) { first = min(first, j); break; }
+  __shared__ int sm[4];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) first = min(first, __shfl_xor(first, o, kWave));
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = first;
+  __syncthreads();
+  if (threadIdx.x == 0) out_len[b] = min(min(sm[0], sm[1]), min(sm[2], sm[3]));
+}
+
+// ---------------------------------------------------------------------------
+// sampler
+// ---------------------------------------------------------------------------
+constexpr int kSampThreads = 1024;
+constexpr int kSampWaves = kSampThreads / kWave;
+constexpr float kFix = 1099511627776.0f;  // 2^40
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Block-wide u64 sum; every thread gets the result.  red: kSampWaves slots.
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t *red) {
+  v = wave_sum_u64(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kSampWaves; ++w) t += red[w];
+  return t;
+}
+
+// One block per row.  logits [M][ld] fp32; u [urows][M] (row of each logits
+// row chosen by gidx[r], clamped to urows - 1, or row 0 when gidx is null).
+__global__ __launch_bounds__(kSampThreads) void sample_top_p_kernel(const float *__restrict__ logits, int64_t ld,
+                                                                    int V, float k2, float top_p,
+                                                                    const float *__restrict__ u, int M, int urows,
+                                                                    const int32_t *__restrict__ gidx,
+                                                                    int32_t *__restrict__ out) {
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float *x = logits + (int64_t)r * ld;
+  __shared__ uint64_t hist[256];
+  __shared__ uint64_t red[kSampWaves];
+  __shared__ float redf[kSampWaves];
+  __shared__ uint64_t sel_mass;   // mass of keys above the selected prefix
+  __shared__ uint32_t sel_digit;
+  __shared__ uint64_t scan_s[kSampWaves];
+  __shared__ uint32_t scan_n[kSampWaves];
+
+  // max
+  float mx = -INFINITY;
+  for (int i = tid; i < V; i += kSampThreads) mx = fmaxf(mx, x[i]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) redf[tid >> 6] = mx;
+  __syncthreads();
+  mx = redf[0];
+#pragma unroll
+  for (int w = 1; w < kSampWaves; ++w) mx = fmaxf(mx, redf[w]);
+
+  auto zkey = [&](int i, uint64_t &q) -> uint32_t {
+    const float z = exp2f((x[i] - mx) * k2);
+    q = (uint64_t)(z * kFix);
+    return __float_as_uint(z);
+  };
+
+  // total mass + first histogram (key bits 31..24)
+  if (tid < 256) hist[tid] = 0;
+  __syncthreads();
+  uint64_t tot = 0;
+  for (int i = tid; i < V; i += kSampThreads) {
+    uint64_t q;
+    const uint32_t key = zkey(i, q);
+    if (q) {
+      tot += q;
+      atomicAdd((unsigned long long *)&hist[key >> 24], (unsigned long long)q);
+    }
+  }
+  const uint64_t Z = block_sum_u64(tot, red);
+
+  // threshold key t* = the largest key with mass(keys >= t*) > top_p * Z,
+  // and the number of tokens with key == t* that stay in the nucleus
+  uint32_t thr = 0;
+  uint64_t above = 0;  // mass of keys > t*
+  uint64_t take = 0xFFFFFFFFull;
+  const bool keep_all = !(top_p < 1.0f);
+  if (!keep_all) {
+    const uint64_t R = (uint64_t)((double)top_p * (double)Z);
+    uint32_t prefix = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      if (pass > 0) {
+        __syncthreads();
+        if (tid < 256) hist[tid] = 0;
+        __syncthreads();
+        const uint32_t pmask = 0xFFFFFFFFu << (shift + 8);
+        for (int i = tid; i < V; i += kSampThreads) {
+          uint64_t q;
+          const uint32_t key = zkey(i, q);
+          if (q && (key & pmask) == prefix)
+            atomicAdd((unsigned long long *)&hist[(key >> shift) & 255], (unsigned long long)q);
+        }
+      }
+      __syncthreads();
+      // wave 0: the largest digit d with above + sum(hist[d..255]) > R
+      if (tid < 64) {
+        uint64_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
+        const uint64_t mine = h0 + h1 + h2 + h3;
+        // suffix sum over lanes tid+1..63
+        uint64_t suf = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint64_t t = __shfl_down(suf, o, kWave);
+          if (tid + o < 64) suf += t;
+        }
+        const uint64_t after = suf - mine;  // mass of digits above this lane's four
+        uint64_t base = above + after;
+        int d = -1;
+        uint64_t dm = 0;
+        // within the lane, from the highest digit down
+        if (base + h3 > R) { d = 4 * tid + 3; dm = base; }
+        else if (base + h3 + h2 > R) { d = 4 * tid + 2; dm = base + h3; }
+        else if (base + h3 + h2 + h1 > R) { d = 4 * tid + 1; dm = base + h3 + h2; }
+        else if (base + mine > R) { d = 4 * tid; dm = base + h3 + h2 + h1; }
+        // the crossing lies in exactly one lane (the suffix mass is monotone)
+        const uint64_t hit = __ballot(d >= 0);
+        const int src = hit ? 63 - __clzll(hit) : 0;
+        if (tid == src) {
+          sel_digit = d >= 0 ? (uint32_t)d : 0u;
+          sel_mass = d >= 0 ? dm : above;
+        }
+      }
+      __syncthreads();
+      prefix |= sel_digit << shift;
+      above = sel_mass;
+    }
+    thr = prefix;
+    // tokens with key == t* all carry q* = floor(2^40 * z(t*)); the first j of
+    // them (by id) are kept, j = floor((R - above) / q*) + 1
+    const uint64_t qs = (uint64_t)(__uint_as_float(thr) * kFix);
+    take = qs ? (R - above) / qs + 1 : 0;
+  }
+
+  // kept mass and draw target
+  // contiguous ranges of 128 ids per thread (1024 * 128 >= V is checked on the host)
+  const int i0 = tid * 128, i1 = min(V, i0 + 128);
+  uint64_t s_keep_gt = 0;  // mass of kept keys > t* in this range
+  uint32_t n_tie = 0;      // tokens with key == t* (and q > 0) in this range
+  for (int i = i0; i < i1; ++i) {
+    uint64_t q;
+    const uint32_t key = zkey(i, q);
+    if (!q) continue;
+    if (keep_all || key > thr) s_keep_gt += q;
+    else if (key == thr) ++n_tie;
+  }
+  // exclusive scans of n_tie (tie rank) and of kept mass (needs tie ranks)
+  const int lane = tid & 63, wv = tid >> 6;
+  uint32_t ninc = n_tie;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(ninc, o, kWave);
+    if (lane >= o) ninc += t;
+  }
+  if (lane == 63) scan_n[wv] = ninc;
+  __syncthreads();
+  uint32_t nbase = 0;
+  for (int w = 0; w < wv; ++w) nbase += scan_n[w];
+  const uint32_t tie0 = nbase + ninc - n_tie;  // rank of this range's first tie
+  const uint64_t qs = keep_all ? 0 : (uint64_t)(__uint_as_float(thr) * kFix);
+  const uint32_t tie_keep = keep_all ? 0u
+                            : (uint32_t)min((uint64_t)n_tie, (take > tie0 ? take - tie0 : 0ull));
+  const uint64_t s_keep = s_keep_gt + (uint64_t)tie_keep * qs;
+  uint64_t sinc = s_keep;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t t = __shfl_up(sinc, o, kWave);
+    if (lane >= o) sinc += t;
+  }
+  if (lane == 63) scan_s[wv] = sinc;
+  __syncthreads();
+  uint64_t sbase = 0, Mk = 0;
+  for (int w = 0; w < kSampWaves; ++w) {
+    if (w < wv) sbase += scan_s[w];
+    Mk += scan_s[w];
+  }
+  const uint64_t pre = sbase + sinc - s_keep;  // kept mass before this range
+
+  const int urow = gidx ? min(max(gidx[r], 0), urows - 1) : 0;
+  const float uu = u[(int64_t)urow * M + r];
+  uint64_t target = (uint64_t)((double)uu * (double)Mk);
+  if (target >= Mk) target = Mk - 1;
+  // the thread whose kept range [pre, pre + s_keep) holds the target walks it
+  if (s_keep && target >= pre && target < pre + s_keep) {
+    uint64_t acc = pre;
+    uint32_t rank = tie0;
+    int pick = i1 - 1;
+    for (int i = i0; i < i1; ++i) {
+      uint64_t q;
+      const uint32_t key = zkey(i, q);
+      if (!q) continue;
+      bool kept;
+      if (keep_all || key > thr) kept = true;
+      else if (key == thr) kept = (uint64_t)(rank++) < take;
+      else kept = false;
+      if (!kept) continue;
+      acc += q;
+      if (acc > target) { pick = i; break; }
+    }
+    out[r] = pick;
+  }
+}
+
+hipError_t launch_gen_fill(const int32_t *prompt, int64_t pstride, int32_t *tokens, int64_t tstride,
+                           const GenLens &lens, int B, hipStream_t s) {
+  hipLaunchKernelGGL(gen_fill_kernel, dim3((unsigned)((tstride + 255) / 256), B), dim3(256), 0, s, prompt, pstride,
+                     tokens, tstride, lens);
+  return hipGetLastError();
+}
+
+hipError_t launch_gen_step(const GenState &st, const GenLens &lens, int B, int eos, const int32_t *prompt,
+                           int64_t pstride, int32_t *tokens, int64_t tstride, int first, hipStream_t s) {
+  hipLaunchKernelGGL(gen_step_kernel, dim3(1), dim3(64), 0, s, st, lens, B, eos, prompt, pstride, tokens, tstride,
+                     first);
+  return hipGetLastError();
+}
+
+hipError_t launch_gen_finish(const GenState &st, int B, int eos, const int32_t *tokens, int64_t tstride,
+                             int32_t *out_len, hipStream_t s) {
+  hipLaunchKernelGGL(gen_finish_kernel, dim3(B), dim3(256), 0, s, st, eos, tokens, tstride, out_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_top_p(const float *logits, int64_t ld, int M, int V, float temperature, float top_p,
+                               const float *u, int urows, const int32_t *gidx, int32_t *out, hipStream_t s) {
+  const float k2 = (float)(1.4426950408889634 / (double)temperature);
+  hipLaunchKernelGGL(sample_top_p_kernel, dim3(M), dim3(kSampThreads), 0, s, logits, ld, V, k2, top_p, u, M, urows,
+                     gidx, out);
+  return hipGetLastError();
+}
+
+}  // namespace llk

@@ -99,6 +99,20 @@ struct DecodeAttnArgs {
   void *out; int out_mode; int64_t out_plane;  // [B][H*hd]: 0 fp32, 2 bf16 hi/lo planes
 };
 
+// Token generation: per-sequence lengths (passed by value) and device state.
+constexpr int kGenMaxBatch = 64;
+struct GenLens {
+  int32_t L[kGenMaxBatch];      // prompt length
+  int32_t total[kGenMaxBatch];  // min(prompt + max_gen, max_seq_len)
+};
+struct GenState {              // each [B] int32 in device memory
+  int32_t *cur, *pos;          // token and position the next decode step feeds
+  int32_t *done, *end;         // finished flag; one past the last written position
+  int32_t *next;               // the step's choice (argmax or sample)
+  int32_t *gidx;               // index of the token the next step produces
+  int32_t *active;             // [1] number of running sequences
+};
+
 hipError_t launch_embed(int dtype, const int32_t *ids, const void *E, float *h, int rows, int D, int V, hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, int mode, const NormArgs &a, int rows, hipStream_t s);
 hipError_t launch_rope_table(float2 *tab, const int32_t *pos, int start_pos, int pos_max, int rows, int hd,
@@ -108,6 +122,16 @@ hipError_t launch_swiglu(const float *gate, const float *up, float *u, int64_t n
 hipError_t launch_argmax_reduce(const float *pv, const int32_t *pi, int rows, int nblk, int32_t *out, hipStream_t s);
 hipError_t launch_argmax_partial(const float *x, int rows, int n, int chunk, float *pv, int32_t *pi, int nblk,
                                  hipStream_t s);
+
+hipError_t launch_gen_fill(const int32_t *prompt, int64_t pstride, int32_t *tokens, int64_t tstride,
+                           const GenLens &lens, int B, hipStream_t s);
+hipError_t launch_gen_step(const GenState &st, const GenLens &lens, int B, int eos, const int32_t *prompt,
+                           int64_t pstride, int32_t *tokens, int64_t tstride, int first, hipStream_t s);
+hipError_t launch_gen_finish(const GenState &st, int B, int eos, const int32_t *tokens, int64_t tstride,
+                             int32_t *out_len, hipStream_t s);
+// One block per row; requires V <= 131072.
+hipError_t launch_sample_top_p(const float *logits, int64_t ld, int M, int V, float temperature, float top_p,
+                               const float *u, int urows, const int32_t *gidx, int32_t *out, hipStream_t s);
 
 hipError_t launch_gemm_bf16(int epi, const GemmArgs &a, hipStream_t s);
 // fp32 path: C = A*B^T (+R), all fp32; epi is EPI_STORE_F32 or EPI_RESID.

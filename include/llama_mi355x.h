@@ -20,7 +20,8 @@
  *   pointers; the library allocates nothing and keeps no pointer after it
  *   returns.  All work is enqueued asynchronously on `stream` (a hipStream_t
  *   passed as void*; NULL is the null stream); outputs are valid once the
- *   stream has completed.  Nothing synchronises the host.
+ *   stream has completed.  Nothing synchronises the host, except
+ *   llama_generate, which waits on its stream to stop early.
  * Layouts: contiguous row-major, device pointers 16-byte aligned.  Linear
  *   weights are [out, in] as in nn.Linear [P2 3.4, 3.5; P1 6.2].  Head h of
  *   wq occupies rows [h*hd, (h+1)*hd) [P1 6.3]; wo's input columns are the
@@ -164,6 +165,69 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
  *   llama_workspace_bytes(a, M, 1)). */
 int lm_head_argmax(const llama_args *a, const float *h, const void *final_norm_w, const void *w_out, int32_t M,
                    float *logits, int32_t *argmax, void *ws, size_t ws_bytes, void *stream);
+
+/* Temperature / top-p sampling of one token per row [P2 6 sample_top_p;
+ * P3 temperature softmax]:
+ *   p = softmax(logits[r] / temperature); the nucleus is the longest prefix
+ *   of the tokens sorted by descending p (ties by ascending id) whose mass
+ *   before each member is at most top_p; out_id[r] is drawn from the
+ *   renormalised nucleus with u[r] in [0, 1) by inverse CDF over the kept
+ *   tokens in ascending id order (the smallest id whose cumulative kept mass
+ *   exceeds u[r] times the kept total).  top_p >= 1 keeps every token.
+ *   Probabilities are carried as floor(2^40 z) with z computed in fp32, and
+ *   every sum is exact, so the choice does not depend on summation order.
+ *   logits [M][V] fp32 (device, finite), u [M] fp32 (device),
+ *   out_id [M] int32 (device).
+ * Errors: ERR_ARG (null pointers, M < 1, V < 1, temperature <= 0, top_p < 0
+ *   or NaN), ERR_UNSUPPORTED (V > 131072). */
+int llama_sample_top_p(const float *logits, int32_t M, int32_t V, float temperature, float top_p, const float *u,
+                       int32_t *out_id, void *stream);
+
+/* Workspace bytes llama_generate needs for `batch` sequences whose prompts
+ * hold at most max_prompt_len tokens; 0 on invalid arguments. */
+size_t llama_generate_workspace_bytes(const llama_args *a, int32_t batch, int32_t max_prompt_len);
+
+#define LLAMA_GEN_NO_GRAPH 1
+
+/* Autoregressive generation [P2 6 generate; P3 4]: each sequence's prompt,
+ * then one model choice per position.
+ *   prompt      [batch][prompt_stride] int32 (device); sequence b's prompt
+ *               is prompt[b][0, prompt_len[b])
+ *   prompt_len  HOST [batch], 1 <= prompt_len[b] <= max_seq_len
+ *   max_gen_len tokens to generate at most per sequence (>= 0); sequence b
+ *               ends at total_b = min(prompt_len[b] + max_gen_len,
+ *               max_seq_len) positions, or right after it produces eos_id
+ *               (eos_id < 0: no end-of-text stop)
+ *   temperature 0: greedy, the argmax with the smallest id on ties;
+ *               > 0: llama_sample_top_p with top_p, drawing the g-th
+ *               generated token of sequence b with uniforms[g][b]
+ *   uniforms    [max_gen_len][batch] fp32 in [0, 1) (device); required when
+ *               temperature > 0, else ignored
+ *   kv          HOST array of n_layers llama_kv (caches of at least `batch`
+ *               rows); rows [0, batch) are overwritten
+ *   tokens      [batch][max_seq_len] int32 (device, out): the prompt and the
+ *               generated tokens, -1 after each sequence's last position
+ *   out_len     [batch] int32 (device, out): the number of tokens before the
+ *               first eos_id in tokens[b] (the pages cut the output there),
+ *               else the sequence's length
+ *   flags       LLAMA_GEN_NO_GRAPH: launch each step's kernels one by one
+ *               instead of replaying a captured HIP graph (graphs also need
+ *               a stream other than the null stream)
+ *   steps_run   HOST (nullable): decode steps run
+ * Prompts of equal length are prefilled together (at most 16384 tokens per
+ * call); then every decode step advances all sequences at once, each at its
+ * own position; a finished sequence keeps its position and its output no
+ * longer changes.  The host waits on the stream every 8 steps and stops once
+ * every sequence has finished.
+ * Errors: ERR_ARG (null pointers, prompt_len out of range, max_gen_len < 0,
+ *   temperature < 0, temperature > 0 without uniforms, prompt_stride <
+ *   max prompt_len), ERR_SHAPE (batch > max_batch_size), ERR_UNSUPPORTED
+ *   (batch > 64, vocab > 131072 when sampling), ERR_WORKSPACE, and the
+ *   errors of llama_prefill / llama_decode_step. */
+int llama_generate(const llama_args *a, const llama_model_w *w, const int32_t *prompt, int32_t prompt_stride,
+                   const int32_t *prompt_len, int32_t batch, int32_t max_gen_len, int32_t eos_id, float temperature,
+                   float top_p, const float *uniforms, const llama_kv *kv, int32_t *tokens, int32_t *out_len,
+                   int32_t flags, int32_t *steps_run, void *ws, size_t ws_bytes, void *stream);
 
 /* Message describing the last non-OK return on the calling thread. */
 const char *llama_last_error(void);

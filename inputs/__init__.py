@@ -70,6 +70,8 @@ def _draw_chunk(kind: str, seed: int, name: str, chunk: int, n: int, param):
         return g.standard_normal(n, dtype=np.float32)
     if kind == "ids":
         return g.integers(0, param, size=n, dtype=np.int32)
+    if kind == "uniform":
+        return g.random(n, dtype=np.float32)
     raise ValueError(kind)
 
 
@@ -133,6 +135,12 @@ def normal_bits(seed: int, name: str, shape, std: float, start: int = 0, stop: O
 def token_ids(seed: int, name: str, shape, vocab: int) -> np.ndarray:
     n = int(np.prod(shape))
     return _draw("ids", seed, name, 0, n, param=vocab, dtype=np.int32).reshape(shape)
+
+
+def uniform(seed: int, name: str, shape) -> np.ndarray:
+    """float32 values uniform in [0, 1) (the draws a sampler consumes)."""
+    n = int(np.prod(shape))
+    return _draw("uniform", seed, name, 0, n).reshape(shape)
 
 
 # ----------------------------------------------------------------------------

@@ -312,3 +312,119 @@ def decode_step(ids, caches: Sequence[Sequence[dict]], embed_rows: Callable, lay
     hf = rms_norm(last, norm_w, args["norm_eps"])
     logits = lm_head(hf, w_out)
     return dict(last_hidden=last, hf=hf, logits=logits, ids=argmax_first(logits))
+
+
+# ---------------------------------------------------------------------------
+# Generation [P2 6 "Inference": generate, sample_top_p; P3 temperature softmax]
+# ---------------------------------------------------------------------------
+def sample_top_p(logits, temperature: float, top_p: float, u: float):
+    """One draw from the top-p nucleus of softmax(logits / temperature).
+
+    Steps in the pages' order [P2 6 sample_top_p]: sort the probabilities in
+    descending order (ties: smaller token id first), take the running sum,
+    drop every token whose mass before it exceeds top_p, renormalise, draw.
+    Reading of the draw (torch.multinomial's use of its random numbers is
+    not stated): inverse CDF with the given uniform u in [0, 1) over the kept
+    tokens in ascending id order, i.e. the smallest id whose cumulative kept
+    probability exceeds u.
+
+    Returns (token, margin): margin is the distance, in probability, of the
+    two decisions from their boundaries (the mass before the tokens next to
+    the cut against top_p, and u against the chosen token's cumulative
+    interval); a computation whose probabilities err by less than the margin
+    makes the same choice.
+    """
+    l = _f64(logits).reshape(-1)
+    p = softmax(l / float(temperature))
+    order = np.argsort(-p, kind="stable")
+    ps = p[order]
+    before = np.cumsum(ps) - ps                # mass ahead of each sorted token
+    removed = before > top_p
+    ks = np.where(removed, 0.0, ps)
+    kept = np.zeros_like(p)
+    kept[order] = ks
+    q = kept / kept.sum()
+    c = np.cumsum(q)
+    tok = int(np.searchsorted(c, u, side="right"))
+    tok = min(tok, int(np.nonzero(q)[0][-1]))
+    # margins
+    # (the first sorted token always has zero mass before it, and the first
+    # and last kept tokens have exact outer boundaries 0 and 1: no margin)
+    if removed.any():
+        k0 = int(np.argmax(removed))           # first removed in sorted order
+        m_cut = before[k0] - top_p
+        if k0 > 1:
+            m_cut = min(m_cut, top_p - before[k0 - 1])
+    else:
+        m_cut = top_p - before[-1] if (top_p < 1.0 and len(p) > 1) else math.inf
+    nz = np.nonzero(q)[0]
+    m_draw = math.inf
+    if tok != nz[0]:
+        m_draw = min(m_draw, u - c[tok - 1])
+    if tok != nz[-1]:
+        m_draw = min(m_draw, c[tok] - u)
+    return tok, float(min(m_cut, m_draw))
+
+
+def generate(prompts, embed_rows: Callable, layer: LayerSource, norm_w, w_out, args: dict, max_gen_len: int,
+             eos_id: int, max_seq_len: int, temperature: float = 0.0, top_p: float = 0.9, uniforms=None,
+             forced=None):
+    """Autoregressive generation of each prompt [P2 6 generate].
+
+    For prompt b of length L the sequence runs to total = min(L + max_gen_len,
+    max_seq_len) positions; position p >= L receives the model's choice from
+    the logits at position p - 1 (argmax when temperature == 0, else
+    ``sample_top_p`` with uniforms[p - L][b]); the sequence stops right after
+    a generated eos_id (the pages' loop ends on the end-of-text token).  The
+    output is cut before the first eos_id anywhere in the sequence, as the
+    pages cut the decoded text.
+
+    The prompt is fed in one forward call and each later token alone; the
+    pages feed the prompt one token at a time, which yields the same cache
+    and the same logits at the prompt's last position.
+
+    ``forced`` (optional, per sequence a token list): the token appended at
+    each generated position is forced[b][p] instead of the oracle's own
+    choice, so that the oracle's choices can be checked along another
+    implementation's path.  Returns, per sequence, dict(tokens, out_len,
+    choices, margins, logits): the appended tokens, the cut length, and for
+    each generated position the oracle's choice, its decision margin (top-2
+    logit gap for argmax, ``sample_top_p``'s margin for sampling) and the
+    logits it was taken from.
+    """
+    out = []
+    for b, prompt in enumerate(prompts):
+        prompt = [int(t) for t in prompt]
+        L = len(prompt)
+        total = min(L + max_gen_len, max_seq_len)
+        toks = list(prompt)
+        choices, margins, step_logits = [], [], []
+        if total > L:
+            caches = [[]]
+            r = prefill(np.array([prompt]), embed_rows, layer, norm_w, w_out, args, caches=caches)
+            logits = r["logits"][0]
+            p = L
+            while True:
+                if temperature == 0.0:
+                    choice = int(argmax_first(logits[None])[0])
+                    margin = float(top2_gap(logits[None])[0])
+                else:
+                    choice, margin = sample_top_p(logits, temperature, top_p, float(uniforms[p - L][b]))
+                tok = int(forced[b][p]) if forced is not None else choice
+                step_logits.append(logits)
+                toks.append(tok)
+                choices.append(choice)
+                margins.append(margin)
+                if (eos_id >= 0 and tok == eos_id) or p + 1 >= total:
+                    break
+                new = []
+                r = decode_step([tok], caches, embed_rows, layer, norm_w, w_out, args, new_kv=new)
+                for (_, l, k, v) in new:
+                    c = caches[0][l]
+                    c["k"] = np.concatenate([c["k"], k[None]], axis=0)
+                    c["v"] = np.concatenate([c["v"], v[None]], axis=0)
+                logits = r["logits"][0]
+                p += 1
+        cut = toks.index(eos_id) if (eos_id >= 0 and eos_id in toks) else len(toks)
+        out.append(dict(tokens=toks, out_len=cut, choices=choices, margins=margins, logits=step_logits))
+    return out

@@ -125,3 +125,53 @@ def test_no_device_reports_hip_error():
     rc = _call_layer(a, ws_bytes=need, ws=ctypes.c_void_p(0x10000))
     assert rc == M.LLAMA_ERR_HIP
     assert M.last_error()
+
+
+def test_sampler_argument_errors():
+    L = M.lib()
+    rc = L.llama_sample_top_p(None, 2, 100, 0.6, 0.9, FAKE, FAKE, None)
+    assert rc == M.LLAMA_ERR_ARG
+    assert L.llama_sample_top_p(FAKE, 0, 100, 0.6, 0.9, FAKE, FAKE, None) == M.LLAMA_ERR_ARG
+    assert L.llama_sample_top_p(FAKE, 2, 100, 0.0, 0.9, FAKE, FAKE, None) == M.LLAMA_ERR_ARG  # T must be > 0
+    assert L.llama_sample_top_p(FAKE, 2, 100, 0.6, -0.1, FAKE, FAKE, None) == M.LLAMA_ERR_ARG
+    assert L.llama_sample_top_p(FAKE, 2, 131073, 0.6, 0.9, FAKE, FAKE, None) == M.LLAMA_ERR_UNSUPPORTED
+
+
+def _gen(a, lens, batch=None, max_gen=4, eos=-1, temp=0.0, uni=FAKE, stride=None, ws_bytes=1 << 40, kv=True):
+    layers = (M.llama_layer_w * 2)(_layer_fake(), _layer_fake())
+    model = M.llama_model_w(0x1000, ctypes.cast(layers, ctypes.POINTER(M.llama_layer_w)), 0x1000, 0x1000)
+    kvs = (M.llama_kv * 2)(M.llama_kv(0x1000, 0x1000), M.llama_kv(0x1000, 0x1000)) if kv else None
+    n = len(lens)
+    arr = (ctypes.c_int32 * max(n, 1))(*lens)
+    steps = ctypes.c_int32(-7)
+    rc = M.lib().llama_generate(ctypes.byref(a), ctypes.byref(model), FAKE, stride or max(lens), arr,
+                                n if batch is None else batch, max_gen, eos, temp, 0.9, uni, kvs, FAKE, FAKE, 0,
+                                ctypes.byref(steps), FAKE, ws_bytes, None)
+    return rc, steps.value
+
+
+def test_generate_argument_errors():
+    a = _args()
+    assert _gen(a, [3, 0])[0] == M.LLAMA_ERR_ARG           # empty prompt
+    assert _gen(a, [3, 65])[0] == M.LLAMA_ERR_ARG          # prompt longer than max_seq_len
+    assert _gen(a, [3, 5], stride=4)[0] == M.LLAMA_ERR_ARG  # stride below the longest prompt
+    assert _gen(a, [3, 5], max_gen=-1)[0] == M.LLAMA_ERR_ARG
+    assert _gen(a, [3, 5], temp=-1.0)[0] == M.LLAMA_ERR_ARG
+    assert _gen(a, [3, 5], temp=0.6, uni=None)[0] == M.LLAMA_ERR_ARG  # sampling needs uniforms
+    assert _gen(a, [3] * 5)[0] == M.LLAMA_ERR_SHAPE         # batch > max_batch_size
+    assert _gen(_args(max_batch_size=128), [3] * 65)[0] == M.LLAMA_ERR_UNSUPPORTED  # batch > 64
+    assert _gen(a, [3, 5], kv=False)[0] == M.LLAMA_ERR_ARG
+    rc, steps = _gen(a, [3, 5], ws_bytes=1024)
+    assert rc == M.LLAMA_ERR_WORKSPACE and steps == -7
+    assert "workspace" in M.last_error()
+
+
+def test_generate_workspace_bytes():
+    a = _args()
+    n1 = M.llama_generate_workspace_bytes(a, 1, 8)
+    n2 = M.llama_generate_workspace_bytes(a, 4, 64)
+    assert 0 < n1 < n2
+    # at least a decode step's and a prefill call's workspace
+    assert n2 >= M.llama_workspace_bytes(a, 4, 64)
+    with pytest.raises(M.LlamaError):
+        M.llama_generate_workspace_bytes(a, 65, 8)

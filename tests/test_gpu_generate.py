@@ -1,0 +1,256 @@
+"""GPU parity of token generation and of the top-p sampler against the oracle
+[P2 6 "Inference": generate, sample_top_p].
+
+Generation is compared along the GPU's own path: the oracle is fed the GPU's
+tokens (``forced``) and reports its own choice and decision margin at every
+generated position; each GPU token must equal the oracle's choice unless the
+margin is below the comparison bar (the argmax gap bar for greedy decoding,
+SAMPLE_MARGIN for sampling).  Stop positions, the -1 padding and the output
+lengths are checked exactly against the pages' stopping rule applied to the
+GPU's tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_decoder_only_rmsnorm_amd as M
+import dense_decoder_only_rmsnorm_amd.runtime as R
+import inputs as I
+from oracle import llama as OL
+from oracle import runner as OR
+
+from gpu_util import BF16_TOL, GAP_EXEMPT, say
+
+pytestmark = pytest.mark.gpu
+
+# Sampler decisions (nucleus cut, inverse-CDF draw) computed from the same
+# fp32 logits: the kernel's probabilities come from fp32 exp2 of fp32
+# products, a = (l - max) * log2(e) / T with |a| <= 40 for every token that
+# carries mass, so each exponent is off by at most ~2e-7 |a| and each
+# probability by at most ~5e-6 relative (far less for the heavy tokens); the
+# cumulative masses the cut and the draw compare are then off by under 5e-6.
+# Below a margin of 2e-5 either choice is accepted.
+SAMPLE_MARGIN = 2e-5
+# Sampling along a generated path: the model's own logits differ from the
+# oracle's by up to ~1e-6 relative (fp32 model), which moves probabilities by
+# a few 1e-6 at temperature 0.6.
+GEN_SAMPLE_MARGIN = 1e-4
+
+
+def _run_generate(dm, args, prompt_np, lens, max_gen, eos, temp=0.0, top_p=0.9, uniforms=None, flags=0,
+                  side_stream=True):
+    B, P = prompt_np.shape
+    cap = args.max_seq_len
+    prompt = torch.from_numpy(prompt_np.astype(np.int32)).cuda()
+    kv = R.kv_caches(dm.cfg, args.n_layers, args.max_batch_size, cap)
+    kva = M.kv_array(kv)
+    tokens = torch.full((B, cap), -7, dtype=torch.int32, device="cuda")
+    out_len = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(M.llama_generate_workspace_bytes(args, B, max(lens)), dtype=torch.uint8, device="cuda")
+    u = None if uniforms is None else torch.from_numpy(np.ascontiguousarray(uniforms, dtype=np.float32)).cuda()
+    torch.cuda.synchronize()
+    if side_stream:
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            steps = M.llama_generate(args, dm.struct, prompt, P, lens, B, max_gen, eos, temp, top_p, u, kva, tokens,
+                                     out_len, flags, ws, s)
+        s.synchronize()
+    else:
+        steps = M.llama_generate(args, dm.struct, prompt, P, lens, B, max_gen, eos, temp, top_p, u, kva, tokens,
+                                 out_len, flags, ws, None)
+        torch.cuda.synchronize()
+    return tokens.cpu().numpy(), out_len.cpu().numpy(), steps
+
+
+def _prefill_logit_error(dm, args, prompt_np, lens, outs):
+    """max |gpu - oracle| of the logits at each prompt's last position (the
+    logits the first generated token is taken from), and the oracle's max |logit|."""
+    err = scale = 0.0
+    for b, L in enumerate(lens):
+        if not outs[b]["logits"]:
+            continue
+        ids = torch.from_numpy(prompt_np[b:b + 1, :L].astype(np.int32)).cuda()
+        logits = torch.empty((1, args.vocab_size), dtype=torch.float32, device="cuda")
+        nxt = torch.empty((1,), dtype=torch.int32, device="cuda")
+        ws = R.workspace(args, 1, L)
+        M.llama_prefill(args, dm.struct, ids, 1, L, None, None, logits, nxt, ws)
+        torch.cuda.synchronize()
+        ref = outs[b]["logits"][0]
+        err = max(err, float(np.max(np.abs(logits.cpu().numpy()[0] - ref))))
+        scale = max(scale, float(np.max(np.abs(ref))))
+    return err, scale
+
+
+def _check_against_oracle(cfg, prompt_np, lens, toks, out_len, max_gen, eos, cap, margin_bar, temp=0.0, top_p=0.9,
+                          uniforms=None, min_decided=0.5, dm=None, args=None):
+    m = OR.model_of(cfg)
+    a = OR.args_of(cfg)
+    prompts = [prompt_np[b, :lens[b]].tolist() for b in range(len(lens))]
+    forced = [toks[b].tolist() for b in range(len(lens))]
+    outs = OL.generate(prompts, lambda r: m.rows("tok_embeddings", r), m.layer, m.get("norm"), m.get("output"), a,
+                       max_gen_len=max_gen, eos_id=eos, max_seq_len=cap, temperature=temp, top_p=top_p,
+                       uniforms=uniforms, forced=forced)
+    if dm is not None:
+        # bf16 models: the GPU's logits carry the error of the bf16 activations
+        # of the prompt's prefill (the pages' activation type) and of the bf16
+        # cache built from them.  If every logit is off by at most e, a top-2
+        # gap above 2e cannot flip; the bar is 2.5e with e measured on the
+        # prompts' last positions, and e itself must meet the bf16 tensor bar.
+        err, scale = _prefill_logit_error(dm, args, prompt_np, lens, outs)
+        say(f"  prompt logits: max err {err:.3e}, max |ref| {scale:.3e}")
+        assert err <= BF16_TOL * scale
+        margin_bar = max(margin_bar, 2.5 * err)
+        say(f"  argmax comparison bar {margin_bar:.3e}")
+    n_gen = n_agree = n_decided = 0
+    for b, o in enumerate(outs):
+        L = lens[b]
+        n = len(o["tokens"])  # the pages' stopping rule along the GPU's tokens
+        assert toks[b, :n].tolist() == o["tokens"], f"seq {b}: prompt or length mismatch"
+        assert np.all(toks[b, n:] == -1), f"seq {b}: tokens written past the stop position"
+        assert out_len[b] == o["out_len"], (b, out_len[b], o["out_len"])
+        for g, (choice, margin) in enumerate(zip(o["choices"], o["margins"])):
+            got = int(toks[b, L + g])
+            n_gen += 1
+            n_decided += margin >= margin_bar
+            n_agree += got == choice
+            if got != choice:
+                assert margin < margin_bar, f"seq {b} gen {g}: gpu {got} vs oracle {choice} (margin {margin:.3e})"
+    say(f"  generated {n_gen}, agree {n_agree}, decided by the margin bar {n_decided}")
+    assert n_gen > 0 and n_decided >= min_decided * n_gen
+    return outs
+
+
+def _c2_setup(cap=48, B=4):
+    cfg = I.CONFIGS["c2"]
+    dm = R.DeviceModel(cfg)
+    args = dm.args
+    args.max_seq_len = cap
+    args.max_batch_size = B
+    return cfg, dm, args
+
+
+def test_generate_greedy_ragged_prompts_graph_and_eager():
+    cfg, dm, args = _c2_setup()
+    lens = [5, 9, 9, 17]
+    prompt = I.token_ids(cfg.seed, "generate_prompt", (4, 17), cfg.vocab_size)
+    say(f"c2 greedy generate, prompts {lens}, 10 new tokens")
+    toks, out_len, steps = _run_generate(dm, args, prompt, lens, 10, -1)
+    assert steps == 9
+    _check_against_oracle(cfg, prompt, lens, toks, out_len, 10, -1, args.max_seq_len, GAP_EXEMPT, dm=dm, args=args)
+    toks2, out_len2, _ = _run_generate(dm, args, prompt, lens, 10, -1, flags=M.LLAMA_GEN_NO_GRAPH)
+    assert np.array_equal(toks, toks2) and np.array_equal(out_len, out_len2)
+    toks3, _, _ = _run_generate(dm, args, prompt, lens, 10, -1, side_stream=False)
+    assert np.array_equal(toks, toks3)
+
+
+def test_generate_greedy_end_of_text_stop():
+    cfg, dm, args = _c2_setup()
+    lens = [6, 11, 3, 8]
+    prompt = I.token_ids(cfg.seed, "generate_prompt_eos", (4, 11), cfg.vocab_size)
+    free, _, _ = _run_generate(dm, args, prompt, lens, 12, -1)
+    # end-of-text id: a token sequence 1 generates at its 4th step and not before
+    row = free[1].tolist()
+    gen = row[lens[1]:lens[1] + 12]
+    eos = next(t for g, t in enumerate(gen) if g >= 3 and t not in row[:lens[1] + g])
+    say(f"c2 greedy generate with end-of-text id {eos}")
+    toks, out_len, steps = _run_generate(dm, args, prompt, lens, 12, eos)
+    for b in range(4):
+        r = free[b].tolist()
+        L = lens[b]
+        gen = r[L:L + 12]
+        stop = gen.index(eos) + 1 if eos in gen else 12  # rows are identical up to the stop
+        assert toks[b, :L + stop].tolist() == r[:L + stop]
+        assert np.all(toks[b, L + stop:] == -1)
+        full = r[:L + stop]
+        assert out_len[b] == (full.index(eos) if eos in full else len(full))
+    _check_against_oracle(cfg, prompt, lens, toks, out_len, 12, eos, args.max_seq_len, GAP_EXEMPT, dm=dm, args=args)
+
+
+def test_generate_edge_cases():
+    cfg, dm, args = _c2_setup(cap=16, B=3)
+    prompt = I.token_ids(cfg.seed, "generate_prompt_edge", (3, 16), cfg.vocab_size)
+    # nothing to generate
+    toks, out_len, steps = _run_generate(dm, args, prompt, [4, 16, 1], 0, -1)
+    assert steps == 0
+    for b, L in enumerate([4, 16, 1]):
+        assert toks[b, :L].tolist() == prompt[b, :L].tolist() and np.all(toks[b, L:] == -1)
+        assert out_len[b] == L
+    # a full-length prompt next to short ones, and an end-of-text id inside a prompt
+    eos = int(prompt[0, 2])
+    toks, out_len, steps = _run_generate(dm, args, prompt, [4, 16, 1], 5, eos)
+    assert toks[1].tolist() == prompt[1].tolist()  # no room: unchanged
+    assert out_len[0] == 2
+    _check_against_oracle(cfg, prompt, [4, 16, 1], toks, out_len, 5, eos, 16, GAP_EXEMPT, min_decided=0.3, dm=dm,
+                          args=args)
+
+
+def test_generate_sampled_fp32_model():
+    cfg = I.CONFIGS["c1"]
+    dm = R.DeviceModel(cfg)
+    args = dm.args
+    args.max_seq_len = 40
+    args.max_batch_size = 3
+    lens = [4, 7, 1]
+    prompt = I.token_ids(cfg.seed, "generate_prompt_sampled", (3, 7), cfg.vocab_size)
+    U = I.uniform(cfg.seed, "generate_uniforms", (16, 3))
+    say("c1 sampled generate T=0.6 top_p=0.9, 16 new tokens")
+    toks, out_len, steps = _run_generate(dm, args, prompt, lens, 16, -1, temp=0.6, top_p=0.9, uniforms=U)
+    _check_against_oracle(cfg, prompt, lens, toks, out_len, 16, -1, 40, GEN_SAMPLE_MARGIN, temp=0.6, top_p=0.9,
+                          uniforms=U.astype(np.float64), min_decided=0.8)
+    toks2, _, _ = _run_generate(dm, args, prompt, lens, 16, -1, temp=0.6, top_p=0.9, uniforms=U,
+                                flags=M.LLAMA_GEN_NO_GRAPH)
+    assert np.array_equal(toks, toks2)
+
+
+# ---------------------------------------------------------------------------
+# the sampler alone, on given logits
+# ---------------------------------------------------------------------------
+SAMPLER_CASES = [
+    # (name, V, rows, logit std, temperature, top_p, integer logits)
+    ("peaked_128k", 128256, 64, 4.0, 0.6, 0.9, False),
+    ("pages_default_32k", 32000, 32, 2.0, 0.6, 0.9, False),
+    ("half_nucleus_32k", 32000, 32, 2.0, 1.0, 0.5, False),
+    ("char_vocab", 68, 64, 1.0, 1.0, 0.9, False),
+    ("keep_all", 1000, 32, 2.0, 0.8, 1.0, False),
+    ("argmax", 4096, 32, 1.0, 0.7, 0.0, False),
+    ("integer_ties", 1000, 32, 2.0, 1.0, 0.6, True),
+    ("max_vocab", 131072, 8, 3.0, 0.6, 0.9, False),
+    ("single_token", 1, 4, 1.0, 1.0, 0.9, False),
+]
+
+
+@pytest.mark.parametrize("case", SAMPLER_CASES, ids=[c[0] for c in SAMPLER_CASES])
+def test_sampler_matches_oracle(case):
+    name, V, rows, std, T, top_p, integer = case
+    say(f"sampler {name}: V={V} rows={rows} T={T} top_p={top_p}")
+    lg = I.normal(11, f"sampler_logits_{name}", (rows, V), std, bf16=False).astype(np.float32)
+    if integer:
+        lg = np.round(lg).astype(np.float32)
+    u = I.uniform(11, f"sampler_u_{name}", (rows,)).astype(np.float32)
+    d_lg = torch.from_numpy(lg).cuda()
+    d_u = torch.from_numpy(u).cuda()
+    out = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+    M.llama_sample_top_p(d_lg, rows, V, T, top_p, d_u, out)
+    got = out.cpu().numpy()
+    out2 = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+    M.llama_sample_top_p(d_lg, rows, V, T, top_p, d_u, out2)
+    assert np.array_equal(got, out2.cpu().numpy()), "not deterministic"
+    decided = agree = 0
+    for r in range(rows):
+        tok, margin = OL.sample_top_p(lg[r].astype(np.float64), T, top_p, float(u[r]))
+        assert 0 <= got[r] < V
+        agree += got[r] == tok
+        if margin >= SAMPLE_MARGIN:
+            decided += 1
+            assert got[r] == tok, f"row {r}: gpu {got[r]} vs oracle {tok} (margin {margin:.3e})"
+        else:
+            # an undecided row still draws from the nucleus (widened by the bar)
+            p = OL.softmax(lg[r].astype(np.float64) / T)
+            ahead = p[p > p[got[r]]].sum() + p[:got[r]][p[:got[r]] == p[got[r]]].sum()
+            assert ahead <= top_p + SAMPLE_MARGIN
+    say(f"  agree {agree}/{rows}, decided {decided}/{rows}")
+    if top_p == 0.0:
+        assert np.array_equal(got, np.argmax(lg, axis=1))
+    # flat distributions put most rows near a boundary; the choices still agree
+    assert decided >= max(1, rows // 8)
+    assert agree >= 0.9 * rows
