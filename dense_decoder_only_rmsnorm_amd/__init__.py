@@ -5,7 +5,8 @@ kernels of ``libllama_mi355x.so`` (built from ``csrc/`` by ``build.py``),
 called through its C ABI (``include/llama_mi355x.h``).  PyTorch supplies
 device memory and streams.  The entry points keep the C names:
 ``llama_layer_forward``, ``llama_prefill``, ``llama_decode_step``,
-``lm_head_argmax``, ``llama_sample_top_p``, ``llama_generate``, plus
+``lm_head_argmax``, ``llama_sample_top_p``, ``llama_generate``,
+``llama_layer_forward_docs``, ``llama_prefill_docs``, plus
 ``llama_ffn_hidden_dim``, ``llama_workspace_bytes`` and
 ``llama_generate_workspace_bytes``.
 
@@ -27,7 +28,8 @@ ERROR_NAMES = {-1: "LLAMA_ERR_ARG", -2: "LLAMA_ERR_SHAPE", -3: "LLAMA_ERR_UNSUPP
                -5: "LLAMA_ERR_HIP"}
 EXPORTED = ("llama_ffn_hidden_dim", "llama_workspace_bytes", "llama_layer_forward", "llama_prefill",
             "llama_decode_step", "lm_head_argmax", "llama_sample_top_p", "llama_generate_workspace_bytes",
-            "llama_generate", "llama_last_error", "llama_timing_enable", "llama_timing_report")
+            "llama_generate", "llama_layer_forward_docs", "llama_prefill_docs", "llama_last_error",
+            "llama_timing_enable", "llama_timing_report")
 LLAMA_GEN_NO_GRAPH = 1
 
 
@@ -87,6 +89,12 @@ def lib() -> ctypes.CDLL:
         L.llama_decode_step.restype = ctypes.c_int
         L.lm_head_argmax.argtypes = [A, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         L.lm_head_argmax.restype = ctypes.c_int
+        L.llama_layer_forward_docs.argtypes = [A, ctypes.POINTER(llama_layer_w), vp, vp, i32, i32, i32,
+                                               ctypes.POINTER(llama_kv), vp, vp, sz, vp]
+        L.llama_layer_forward_docs.restype = ctypes.c_int
+        L.llama_prefill_docs.argtypes = [A, ctypes.POINTER(llama_model_w), vp, vp, i32, i32, ctypes.POINTER(llama_kv),
+                                         vp, vp, vp, vp, sz, vp]
+        L.llama_prefill_docs.restype = ctypes.c_int
         L.llama_sample_top_p.argtypes = [vp, i32, i32, ctypes.c_float, ctypes.c_float, vp, vp, vp]
         L.llama_sample_top_p.restype = ctypes.c_int
         L.llama_generate_workspace_bytes.argtypes = [A, i32, i32]
@@ -177,6 +185,26 @@ def llama_layer_forward(args: llama_args, layer: dict, x, y, batch: int, seq_len
     _check(rc)
 
 
+def llama_layer_forward_docs(args: llama_args, layer: dict, x, y, batch: int, seq_len: int, start_pos: int = 0,
+                             kv=None, doc_ids=None, ws=None, stream=None):
+    """``doc_ids``: int32 device tensor [batch, start_pos + seq_len] (document-level mask) or None."""
+    lw = layer_struct(layer)
+    kvs = llama_kv(_p(kv[0]), _p(kv[1])) if kv is not None else None
+    rc = lib().llama_layer_forward_docs(ctypes.byref(args), ctypes.byref(lw), _p(x), _p(y), batch, seq_len,
+                                        start_pos, ctypes.byref(kvs) if kvs is not None else None, _p(doc_ids),
+                                        _p(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc)
+
+
+def llama_prefill_docs(args: llama_args, model, ids, doc_ids, batch: int, seq_len: int, kv=None, hidden=None,
+                       logits=None, next_id=None, ws=None, stream=None):
+    m = model[0]
+    rc = lib().llama_prefill_docs(ctypes.byref(args), ctypes.byref(m), _p(ids), _p(doc_ids), batch, seq_len,
+                                  kv if kv is not None else None, _p(hidden), _p(logits), _p(next_id), _p(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc)
+
+
 def llama_prefill(args: llama_args, model, ids, batch: int, seq_len: int, kv=None, hidden=None, logits=None,
                   next_id=None, ws=None, stream=None):
     """``model`` is a (llama_model_w, keep-alive) pair from model_struct; kv a kv_array or None."""
@@ -248,4 +276,5 @@ __all__ = ["llama_timing_enable", "llama_timing_report", "lib", "last_error", "L
            "make_args", "layer_struct", "model_struct", "kv_array", "llama_ffn_hidden_dim",
            "llama_workspace_bytes", "llama_layer_forward", "llama_prefill", "llama_decode_step", "lm_head_argmax",
            "llama_sample_top_p", "llama_generate_workspace_bytes", "llama_generate", "LLAMA_GEN_NO_GRAPH",
+           "llama_layer_forward_docs", "llama_prefill_docs",
            "LLAMA_F32", "LLAMA_BF16", "EXPORTED"]

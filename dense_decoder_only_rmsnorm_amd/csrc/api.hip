@@ -184,11 +184,13 @@ struct PrefillWs {
   float *pval;
   int32_t *pidx;
   int nblk;
+  int32_t *kv_lo;  // [B][S] lowest visible key per query (document mask)
 };
 
 PrefillWs carve_prefill(Carver &c, const Dims &d, int B, int S) {
   PrefillWs w{};
   const size_t T = (size_t)B * S;
+  w.kv_lo = c.take<int32_t>(T);
   w.h = c.take<float>(T * d.D);
   w.tab = c.take<float2>((size_t)S * (d.hd / 2));
   if (d.dt == LLAMA_BF16) {
@@ -355,7 +357,7 @@ int run_head(const Dims &d, const HeadWs &hw, const void *w_out, int M, float *l
 // copy-free residual epilogues); x_in is the layer input (may equal h).
 int run_layer_prefill(const llama_args *a, const Dims &d, const llama_layer_w *lw, const float *x_in, float *h,
                       int B, int S, int start_pos, const llama_kv *kv, const PrefillWs &w, bool table_ready,
-                      hipStream_t s) {
+                      const int32_t *kv_lo, hipStream_t s) {
   const int T = B * S;
   const int cap = kv ? a->max_seq_len : S;
   void *kc = kv ? kv->k : w.k;
@@ -436,6 +438,7 @@ int run_layer_prefill(const llama_args *a, const Dims &d, const llama_layer_w *l
   at.hd = d.hd;
   at.start_pos = start_pos;
   at.scale = (float)(1.0 / sqrt((double)d.hd));
+  at.kv_lo = kv_lo;
   LAUNCH("attn_prefill", launch_attn_prefill(d.dt, at, s));
 
   if (d.dt == LLAMA_BF16) {
@@ -570,6 +573,12 @@ size_t llama_workspace_bytes(const llama_args *a, int32_t batch, int32_t seq_len
 int llama_layer_forward(const llama_args *a, const llama_layer_w *w, const float *x, float *y, int32_t batch,
                         int32_t seq_len, int32_t start_pos, const llama_kv *kv, void *ws, size_t ws_bytes,
                         void *stream) {
+  return llama_layer_forward_docs(a, w, x, y, batch, seq_len, start_pos, kv, nullptr, ws, ws_bytes, stream);
+}
+
+int llama_layer_forward_docs(const llama_args *a, const llama_layer_w *w, const float *x, float *y, int32_t batch,
+                             int32_t seq_len, int32_t start_pos, const llama_kv *kv, const int32_t *doc_ids, void *ws,
+                             size_t ws_bytes, void *stream) {
   Dims d;
   if (int e = check_model(a, d)) return e;
   if (int e = check_layer_w(w)) return e;
@@ -590,12 +599,20 @@ int llama_layer_forward(const llama_args *a, const llama_layer_w *w, const float
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carver c(ws);
   PrefillWs pw = carve_prefill(c, d, batch, seq_len);
-  return run_layer_prefill(a, d, w, x, y, batch, seq_len, start_pos, kv, pw, false, s);
+  if (doc_ids) LAUNCH("doc_starts", launch_doc_starts(doc_ids, batch, start_pos, seq_len, pw.kv_lo, s));
+  return run_layer_prefill(a, d, w, x, y, batch, seq_len, start_pos, kv, pw, false, doc_ids ? pw.kv_lo : nullptr,
+                           s);
 }
 
 int llama_prefill(const llama_args *a, const llama_model_w *w, const int32_t *ids, int32_t batch, int32_t seq_len,
                   const llama_kv *kv, float *hidden, float *logits, int32_t *next_id, void *ws, size_t ws_bytes,
                   void *stream) {
+  return llama_prefill_docs(a, w, ids, nullptr, batch, seq_len, kv, hidden, logits, next_id, ws, ws_bytes, stream);
+}
+
+int llama_prefill_docs(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *doc_ids,
+                       int32_t batch, int32_t seq_len, const llama_kv *kv, float *hidden, float *logits,
+                       int32_t *next_id, void *ws, size_t ws_bytes, void *stream) {
   Dims d;
   if (int e = check_model(a, d)) return e;
   if (!w || !w->tok_embeddings || !w->norm || !w->output || (d.L > 0 && !w->layers))
@@ -623,9 +640,11 @@ int llama_prefill(const llama_args *a, const llama_model_w *w, const int32_t *id
   // a1: embedding rows
   LAUNCH("embed", launch_embed(d.dt, ids, w->tok_embeddings, h, T, d.D, d.V, s));
   LAUNCH("rope_table", launch_rope_table(pw.tab, nullptr, 0, INT32_MAX, seq_len, d.hd, a->rope_theta, s));
+  if (doc_ids) LAUNCH("doc_starts", launch_doc_starts(doc_ids, batch, 0, seq_len, pw.kv_lo, s));
   // a2-a11: layers
   for (int l = 0; l < d.L; ++l) {
-    if (int e = run_layer_prefill(a, d, &w->layers[l], h, h, batch, seq_len, 0, kv ? &kv[l] : nullptr, pw, true, s))
+    if (int e = run_layer_prefill(a, d, &w->layers[l], h, h, batch, seq_len, 0, kv ? &kv[l] : nullptr, pw, true,
+                                  doc_ids ? pw.kv_lo : nullptr, s))
       return e;
   }
   // a12: final norm of each sequence's last row -> hi/lo (bf16) or fp32

@@ -51,6 +51,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(AttnArgs a) {
   const bool valid = s < a.S;
   const int h = g * n_rep + r_head;
   const int qp = a.start_pos + (valid ? s : a.S - 1);
+  const int qlo = a.kv_lo ? min(max(a.kv_lo[(int64_t)b * a.S + (valid ? s : a.S - 1)], 0), qp) : 0;
   const int gk = lane >> 5;
 
   const u16 *Q = static_cast<const u16 *>(a.q);
@@ -111,19 +112,22 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(AttnArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + kb * 32 + 8 * (r / 4) + 4 * gk + (r % 4);
         float v = sc[kb][r] * c;
-        v = key <= qp ? v : -INFINITY;
+        v = (key <= qp && key >= qlo) ? v : -INFINITY;
         sc[kb][r] = v;
         tmax = fmaxf(tmax, v);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
     const float m_new = fmaxf(m, tmax);
-    const float alpha = exp2f(m - m_new);  // m == -inf on the first tile: alpha = 0
+    // m_new stays -inf while every key so far is masked (keys before the
+    // query's document); 0 stands in for it so that those weights are 0
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m - m_use);  // m == -inf before the first visible key: alpha = 0
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(sc[kb][r] - m_new);
+        const float p = exp2f(sc[kb][r] - m_use);
         sc[kb][r] = p;
         rs += p;
       }
@@ -203,6 +207,10 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(AttnArgs a) {
 // blocks one XCD receives (ids congruent mod 8) share a group's K/V in L2;
 // within a group the longest causal ranges start first.
 // ---------------------------------------------------------------------------
+// DOC: queries also have a lowest visible key (document mask); the block
+// starts at the tile of its lowest bound and each wave classifies tiles by
+// its own bounds.
+template <bool DOC>
 __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
   constexpr int HD = 128;
   constexpr int KT = 64;            // keys per tile
@@ -231,6 +239,19 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
   const int qpos = a.start_pos + srow;
   const int wmax = (int)wave_max((float)qpos);
   const int wmin = -(int)wave_max((float)-qpos);
+  int qlo = 0, wlo_min = 0, wlo_max = 0, kt_first = 0;
+  if (DOC) {
+    __shared__ int blo[8];
+    qlo = min(max(a.kv_lo[(int64_t)b * a.S + srow], 0), qpos);
+    wlo_max = (int)wave_max((float)qlo);
+    wlo_min = -(int)wave_max((float)-qlo);
+    if (lane == 0) blo[wave] = wlo_min;
+    __syncthreads();
+    int mn = blo[0];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) mn = min(mn, blo[w]);
+    kt_first = mn / 64;
+  }
 
   // Q fragments (B operand of S^T = K Q^T): row rho, head-dim 16t + 8*hf .. +7
   bf16x8 qf[NT];
@@ -326,14 +347,18 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
       for (int r = 0; r < 16; ++r) {
         if (MASK) {
           const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key > qpos) sc[kb][r] = -INFINITY;
+          if (key > qpos || (DOC && key < qlo)) sc[kb][r] = -INFINITY;
         }
         mx = fmaxf(mx, sc[kb][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;
     if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
-      const float m_new = fmaxf(m, mx);  // finite: key 0 is visible to every query
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      // finite where the lane has a visible key so far (always without
+      // documents: key 0 is visible to every query)
+      const float m_new = fmaxf(m, mx);
+      float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      // a lane still without a visible key keeps m = -inf (and l = o = 0)
+      if (DOC && m_new == -INFINITY) alpha = 1.f;
       l *= alpha;
       m = m_new;
 #pragma unroll
@@ -346,7 +371,9 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -m));
+        float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -m));
+        // a lane with no visible key yet has m = -inf: its masked scores weigh 0
+        if (DOC && MASK && sc[kb][r] == -INFINITY) p = 0.f;
         sc[kb][r] = p;
         rs += p;
       }
@@ -383,14 +410,23 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
   // masked, and tiles past the wave's last query are skipped.  Every wave
   // passes the same ntiles barriers.
   const int nfull = min(ntiles, (wmin + 1) / KT);
-  issue(0, 0);
-  for (int kt = 0; kt < ntiles; ++kt) {
+  issue(kt_first, kt_first & 1);
+  for (int kt = kt_first; kt < ntiles; ++kt) {
     __syncthreads();  // tile kt has landed; every wave is done with tile kt-1
     if (kt + 1 < ntiles) issue(kt + 1, (kt + 1) & 1);
-    if (kt < nfull)
+    if (DOC) {
+      // skip tiles wholly below the wave's lowest bound or past its last query
+      const int k0 = kt * KT;
+      if (k0 + KT - 1 < wlo_min || k0 > wmax) continue;
+      if (k0 >= wlo_max && kt < nfull)
+        tile(kt, std::integral_constant<bool, false>());
+      else
+        tile(kt, std::integral_constant<bool, true>());
+    } else if (kt < nfull) {
       tile(kt, std::integral_constant<bool, false>());
-    else if (kt * KT <= wmax)
+    } else if (kt * KT <= wmax) {
       tile(kt, std::integral_constant<bool, true>());
+    }
   }
 
   // lane holds O^T[d = 32*ob + 8*(r/4) + 4*hf + r%4][query lane%32]
@@ -426,6 +462,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(AttnArgs a) {
   const int s = qblk * 64 + lane;
   const bool valid = s < a.S;
   const int qp = a.start_pos + (valid ? s : a.S - 1);
+  const int qlo = a.kv_lo ? min(max(a.kv_lo[(int64_t)b * a.S + (valid ? s : a.S - 1)], 0), qp) : 0;
   const float *qrow = static_cast<const float *>(a.q) + (int64_t)(b * a.S + (valid ? s : a.S - 1)) * a.q_stride + h * HD;
   float q[HD], o[HD];
 #pragma unroll
@@ -446,6 +483,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(AttnArgs a) {
     for (int j = 0; j < KT; ++j) {
       const int key = k0 + j;
       if (key > qp) break;
+      if (key < qlo) continue;
       float dot = 0.f;
 #pragma unroll
       for (int d = 0; d < HD; ++d) dot = fmaf(q[d], Ks[j][d], dot);
@@ -990,7 +1028,10 @@ hipError_t prefill_hd(int dtype, const AttnArgs &a, hipStream_t s) {
   if (dtype == 1 && HD == 128) {
     const int QB = 256 / (a.H / a.G);
     const int nblk = ((a.S + QB - 1) / QB) * a.G * a.B;
-    hipLaunchKernelGGL(attn_fwd_w8, dim3(nblk), dim3(512), 0, s, a);
+    if (a.kv_lo)
+      hipLaunchKernelGGL(attn_fwd_w8<true>, dim3(nblk), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL(attn_fwd_w8<false>, dim3(nblk), dim3(512), 0, s, a);
   } else if (dtype == 1) {
     const int QB = 128 / (a.H / a.G);
     dim3 grid((a.S + QB - 1) / QB, a.G, a.B);
@@ -1029,6 +1070,44 @@ hipError_t launch_attn_prefill(int dtype, const AttnArgs &a, hipStream_t s) {
     case 128: return prefill_hd<128>(dtype, a, s);
   }
   return hipErrorInvalidValue;
+}
+
+// Document starts: an inclusive max-scan of the run-start positions
+// (p where doc[p] != doc[p-1], and 0).  One block per sequence.
+__global__ __launch_bounds__(1024) void doc_starts_kernel(const int32_t *__restrict__ doc, int start_pos, int S,
+                                                          int32_t *__restrict__ kv_lo) {
+  const int b = blockIdx.x;
+  const int n = start_pos + S;
+  const int32_t *d = doc + (int64_t)b * n;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int wm[16];
+  __shared__ int carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < n; base += 1024) {
+    const int p = base + threadIdx.x;
+    int v = 0;
+    if (p < n) v = (p == 0 || d[p] != d[p - 1]) ? p : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(v, o, kWave);
+      if (lane >= o) v = max(v, t);
+    }
+    if (lane == 63) wm[wave] = v;
+    __syncthreads();
+    int pre = carry;
+    for (int w = 0; w < wave; ++w) pre = max(pre, wm[w]);
+    v = max(v, pre);
+    if (p >= start_pos && p < n) kv_lo[(int64_t)b * S + (p - start_pos)] = v;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry = v;
+    __syncthreads();
+  }
+}
+
+hipError_t launch_doc_starts(const int32_t *doc, int B, int start_pos, int S, int32_t *kv_lo, hipStream_t s) {
+  hipLaunchKernelGGL(doc_starts_kernel, dim3(B), dim3(1024), 0, s, doc, start_pos, S, kv_lo);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_combine(const DecodeAttnArgs &a, hipStream_t s) {

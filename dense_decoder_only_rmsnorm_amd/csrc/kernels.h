@@ -81,6 +81,9 @@ struct AttnArgs {
   int B, S, H, G, hd;
   int start_pos;                          // absolute position of query s = start_pos + s
   float scale;                            // 1/sqrt(hd)
+  // optional [B][S] int32: the lowest key position query s may attend to
+  // (document mask); keys below it get zero weight.  nullptr: 0.
+  const int32_t *kv_lo;
 };
 
 // Decode attention over the cache (split over key chunks, then combined).
@@ -142,6 +145,9 @@ int skinny_nblk(int N, int epi);
 hipError_t launch_skinny(int epi, const SkinnyArgs &a, hipStream_t s);
 
 hipError_t launch_attn_prefill(int dtype, const AttnArgs &a, hipStream_t s);
+// kv_lo[b][s] = first position of the document (maximal run of equal ids in
+// doc[b][0, start_pos + S)) that holds position start_pos + s.
+hipError_t launch_doc_starts(const int32_t *doc, int B, int start_pos, int S, int32_t *kv_lo, hipStream_t s);
 hipError_t launch_attn_decode(int dtype, const DecodeAttnArgs &a, hipStream_t s);
 hipError_t launch_attn_combine(const DecodeAttnArgs &a, hipStream_t s);
 

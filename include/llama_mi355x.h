@@ -124,6 +124,21 @@ int llama_layer_forward(const llama_args *a, const llama_layer_w *w, const float
                         int32_t batch, int32_t seq_len, int32_t start_pos, const llama_kv *kv,
                         void *ws, size_t ws_bytes, void *stream);
 
+/* llama_layer_forward with the document-level attention mask [P2 appendix,
+ * item 1 (document-level attention mask); P2 1 (the cross-document mask among
+ * Llama 3's changes)]: when several documents are concatenated into one
+ * sequence, a token attends only to earlier tokens of its own document.
+ *   doc_ids [batch][start_pos + seq_len] int32 (device, nullable): a
+ *     document id per position, cache positions included; a document is a
+ *     maximal run of equal ids, so key j is visible to the query at position
+ *     p iff j <= p and positions j..p all carry the same id.  RoPE positions
+ *     stay the positions in the concatenated sequence.  NULL: plain causal
+ *     mask (llama_layer_forward).
+ * Errors: as llama_layer_forward. */
+int llama_layer_forward_docs(const llama_args *a, const llama_layer_w *w, const float *x, float *y,
+                             int32_t batch, int32_t seq_len, int32_t start_pos, const llama_kv *kv,
+                             const int32_t *doc_ids, void *ws, size_t ws_bytes, void *stream);
+
 /* Prefill of `batch` sequences of `seq_len` tokens from position 0
  * [P2 4 Transformer.forward; P1 4-12]: embedding lookup, n_layers blocks,
  * final RMSNorm of each sequence's last position, LM head, argmax.
@@ -139,6 +154,13 @@ int llama_layer_forward(const llama_args *a, const llama_layer_w *w, const float
 int llama_prefill(const llama_args *a, const llama_model_w *w, const int32_t *ids, int32_t batch,
                   int32_t seq_len, const llama_kv *kv, float *hidden, float *logits, int32_t *next_id,
                   void *ws, size_t ws_bytes, void *stream);
+
+/* llama_prefill with the document-level attention mask (see
+ * llama_layer_forward_docs): doc_ids [batch][seq_len] int32 (device,
+ * nullable; NULL = llama_prefill).  Errors: as llama_prefill. */
+int llama_prefill_docs(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *doc_ids,
+                       int32_t batch, int32_t seq_len, const llama_kv *kv, float *hidden, float *logits,
+                       int32_t *next_id, void *ws, size_t ws_bytes, void *stream);
 
 /* One decode step: one new token per sequence [P2 3.3, 6 generate].
  *   ids [batch] int32 (device): the new tokens

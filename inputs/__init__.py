@@ -143,6 +143,17 @@ def uniform(seed: int, name: str, shape) -> np.ndarray:
     return _draw("uniform", seed, name, 0, n).reshape(shape)
 
 
+def document_ids(seed: int, name: str, batch: int, seq_len: int, max_doc: int) -> np.ndarray:
+    """int32 [batch, seq_len] document ids for sequences packed from documents
+    of seeded lengths uniform in [1, max_doc]: ids 0, 1, 2, ... per run."""
+    out = np.empty((batch, seq_len), dtype=np.int32)
+    for b in range(batch):
+        lens = _draw("ids", seed, f"{name}/{b}", 0, seq_len, param=max_doc, dtype=np.int32) + 1
+        ids = np.repeat(np.arange(seq_len, dtype=np.int32), lens)[:seq_len]
+        out[b] = ids
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Configurations (shapes, dtypes, seeds; no derived quantities of the method)
 # ----------------------------------------------------------------------------

@@ -133,6 +133,23 @@ def causal_mask(q_positions, k_positions) -> np.ndarray:
     return np.where(kp > qp, -np.inf, 0.0)
 
 
+def document_mask(q_positions, k_positions, doc_ids) -> np.ndarray:
+    """The document-level causal mask [P2 appendix item 1; P2 1, the
+    cross-document mask]: 0 where the key is at or before the query AND in
+    the same document, -inf elsewhere.  Documents are concatenated into one
+    sequence, so a document is a maximal run of equal ids; ``doc_ids`` gives
+    the id at every absolute position up to the last query.
+    """
+    doc = np.asarray(doc_ids).reshape(-1)
+    run = np.zeros(len(doc), dtype=np.int64)  # index of the run each position lies in
+    for p in range(1, len(doc)):
+        run[p] = run[p - 1] + (1 if doc[p] != doc[p - 1] else 0)
+    qp = np.asarray(q_positions)
+    kp = np.asarray(k_positions)
+    visible = (kp[None, :] <= qp[:, None]) & (run[kp][None, :] == run[qp][:, None])
+    return np.where(visible, 0.0, -np.inf)
+
+
 def softmax(s, axis=-1) -> np.ndarray:
     """exp(s - max) / sum(exp(s - max)); entries at -inf get weight 0."""
     s = _f64(s)
@@ -141,8 +158,9 @@ def softmax(s, axis=-1) -> np.ndarray:
     return e / np.sum(e, axis=axis, keepdims=True)
 
 
-def attention(q, k, v, q_positions, k_positions, return_probs: bool = False):
-    """Causal GQA attention for one sequence.
+def attention(q, k, v, q_positions, k_positions, return_probs: bool = False, doc_ids=None):
+    """Causal GQA attention for one sequence (with ``doc_ids``: under the
+    document-level mask, ``document_mask``).
 
     q: [S, H, hd]; k, v: [L, G, hd] (keys already rotated).  For head h the
     KV head is g = h // (H // G) [P1 8, `head//4`; P2 3.4 repeat_kv].
@@ -155,7 +173,10 @@ def attention(q, k, v, q_positions, k_positions, return_probs: bool = False):
     S, H, hd = q.shape
     G = k.shape[1]
     n_rep = H // G
-    mask = causal_mask(q_positions, k_positions)
+    if doc_ids is None:
+        mask = causal_mask(q_positions, k_positions)
+    else:
+        mask = document_mask(q_positions, k_positions, doc_ids)
     out = np.empty((S, H, hd), dtype=F64)
     probs = []
     for h in range(H):
@@ -188,7 +209,8 @@ def feed_forward(xn, w1, w2, w3) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # a2-a11: one decoder layer
 # ---------------------------------------------------------------------------
-def layer_forward(h, lw: dict, args: dict, positions, cache: Optional[dict] = None, taps: Optional[dict] = None):
+def layer_forward(h, lw: dict, args: dict, positions, cache: Optional[dict] = None, taps: Optional[dict] = None,
+                  doc_ids=None):
     """One pre-norm decoder block on one sequence [P2 3.6; P1 6-10].
 
     h: [S, D] hidden states entering the layer; positions: the S absolute
@@ -219,7 +241,10 @@ def layer_forward(h, lw: dict, args: dict, positions, cache: Optional[dict] = No
         k_pos = np.arange(k_all.shape[0])
     else:
         k_all, v_all, k_pos = k, v, positions
-    o = attention(q, k_all, v_all, positions, k_pos)
+    if doc_ids is None:
+        o = attention(q, k_all, v_all, positions, k_pos)
+    else:
+        o = attention(q, k_all, v_all, positions, k_pos, doc_ids=doc_ids)
     attn_out = o @ _f64(lw["wo"]).T
     h1 = h + attn_out
     xn2 = rms_norm(h1, lw["ffn_norm"], eps)
@@ -257,13 +282,14 @@ LayerSource = Callable[[int], dict]
 
 
 def prefill(ids, embed_rows: Callable, layer: LayerSource, norm_w, w_out, args: dict,
-            caches: Optional[list] = None, all_hidden: bool = False):
+            caches: Optional[list] = None, all_hidden: bool = False, doc_ids=None):
     """Prefill of a batch of sequences from position 0 [P2 4 Transformer.forward; P1 4-12].
 
     ids: [B, S] int.  ``embed_rows(ids_1d)`` returns embedding rows;
     ``layer(l)`` returns layer l's weights (streamed, one layer at a time).
     When ``caches`` is a list of B lists (one per sequence), each layer's
     keys/values are appended to caches[b][l] (dicts with "k"/"v").
+    ``doc_ids`` [B, S] (optional) applies the document-level mask.
     Returns dict(hidden=[B,S,D] or last rows, hf=[B,D], logits=[B,V], ids=[B]).
     """
     ids = np.asarray(ids)
@@ -277,7 +303,10 @@ def prefill(ids, embed_rows: Callable, layer: LayerSource, norm_w, w_out, args: 
             if caches is not None:
                 cache = {"k": np.zeros((0, args["n_kv_heads"], args["dim"] // args["n_heads"])),
                          "v": np.zeros((0, args["n_kv_heads"], args["dim"] // args["n_heads"]))}
-            hs[b] = layer_forward(hs[b], lw, args, positions, cache=cache)
+            if doc_ids is None:
+                hs[b] = layer_forward(hs[b], lw, args, positions, cache=cache)
+            else:
+                hs[b] = layer_forward(hs[b], lw, args, positions, cache=cache, doc_ids=np.asarray(doc_ids)[b])
             if caches is not None:
                 caches[b].append(cache)
     last = np.stack([hs[b][-1] for b in range(B)])

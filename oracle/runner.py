@@ -22,7 +22,7 @@ def model_of(cfg: I.Config) -> I.SyntheticModel:
 
 
 def prefill(cfg: I.Config, ids: Optional[np.ndarray] = None, n_layers: Optional[int] = None,
-            all_hidden: bool = False, caches: Optional[list] = None) -> dict:
+            all_hidden: bool = False, caches: Optional[list] = None, doc_ids: Optional[np.ndarray] = None) -> dict:
     """Oracle prefill of ``cfg`` (ids default to the seeded prompt)."""
     m = model_of(cfg)
     ids = I.prompt_ids(cfg) if ids is None else np.asarray(ids)
@@ -30,16 +30,16 @@ def prefill(cfg: I.Config, ids: Optional[np.ndarray] = None, n_layers: Optional[
     if n_layers is not None:
         a["n_layers"] = n_layers
     return L.prefill(ids, lambda r: m.rows("tok_embeddings", r), m.layer, m.get("norm"), m.get("output"), a,
-                     caches=caches, all_hidden=all_hidden)
+                     caches=caches, all_hidden=all_hidden, doc_ids=doc_ids)
 
 
 def layer(cfg: I.Config, x: Optional[np.ndarray] = None, layer_index: int = 0, rows: Optional[Sequence[int]] = None,
-          taps: bool = False) -> dict:
+          taps: bool = False, doc_ids: Optional[np.ndarray] = None) -> dict:
     """Oracle output of one layer on hidden states x [B, S, D] at positions 0..S-1.
 
     ``rows`` restricts the output to the given positions (each still attends
     to all earlier positions; later positions are not computed beyond their
-    keys and values).
+    keys and values).  ``doc_ids`` [B, S] applies the document-level mask.
     """
     m = model_of(cfg)
     x = I.hidden_x(cfg) if x is None else np.asarray(x)
@@ -48,19 +48,23 @@ def layer(cfg: I.Config, x: Optional[np.ndarray] = None, layer_index: int = 0, r
     B, S, _ = x.shape
     outs, tap_list = [], []
     for b in range(B):
+        docs = None if doc_ids is None else np.asarray(doc_ids)[b]
         if rows is None:
             t = {} if taps else None
-            outs.append(L.layer_forward(x[b], lw, a, np.arange(S), taps=t))
+            if docs is None:
+                outs.append(L.layer_forward(x[b], lw, a, np.arange(S), taps=t))
+            else:
+                outs.append(L.layer_forward(x[b], lw, a, np.arange(S), taps=t, doc_ids=docs))
             tap_list.append(t)
         else:
-            outs.append(_layer_rows(x[b], lw, a, rows))
+            outs.append(_layer_rows(x[b], lw, a, rows, docs))
     res = dict(y=np.stack(outs))
     if taps:
         res["taps"] = tap_list
     return res
 
 
-def _layer_rows(x: np.ndarray, lw: dict, a: dict, rows: Sequence[int]) -> np.ndarray:
+def _layer_rows(x: np.ndarray, lw: dict, a: dict, rows: Sequence[int], doc_ids=None) -> np.ndarray:
     """Layer outputs at the given rows only: keys/values of all earlier rows are
     computed by the oracle's own projections, then each requested row is run as
     a one-token step over that prefix (the KV-cache identity of P2 3.3)."""
@@ -74,7 +78,10 @@ def _layer_rows(x: np.ndarray, lw: dict, a: dict, rows: Sequence[int]) -> np.nda
     out = []
     for r in rows:
         cache = {"k": k[:r], "v": v[:r]}
-        out.append(L.layer_forward(x[r:r + 1], lw, a, np.array([r]), cache=cache)[0])
+        if doc_ids is None:
+            out.append(L.layer_forward(x[r:r + 1], lw, a, np.array([r]), cache=cache)[0])
+        else:
+            out.append(L.layer_forward(x[r:r + 1], lw, a, np.array([r]), cache=cache, doc_ids=doc_ids[:r + 1])[0])
     return np.stack(out)
 
 

@@ -17,7 +17,22 @@ from oracle import llama as L
 
 _orig = {n: getattr(L, n) for n in ("rope_frequencies", "apply_rope", "attention", "causal_mask", "rms_norm",
                                     "feed_forward", "layer_forward", "argmax_first", "silu", "softmax",
-                                    "ffn_hidden_dim", "lm_head")}
+                                    "ffn_hidden_dim", "lm_head", "document_mask")}
+
+
+def _docmask_same_id(q_positions, k_positions, doc_ids):
+    # treats equal ids as one document even when another document lies between
+    doc = np.asarray(doc_ids).reshape(-1)
+    qp, kp = np.asarray(q_positions), np.asarray(k_positions)
+    vis = (kp[None, :] <= qp[:, None]) & (doc[kp][None, :] == doc[qp][:, None])
+    return np.where(vis, 0.0, -np.inf)
+
+
+def _docmask_strict_diagonal(q_positions, k_positions, doc_ids):
+    # drops the query's own key
+    m = _orig["document_mask"](q_positions, k_positions, doc_ids)
+    qp, kp = np.asarray(q_positions), np.asarray(k_positions)
+    return np.where(kp[None, :] == qp[:, None], -np.inf, m)
 
 
 def _rope_freq_no_two(hd, theta):
@@ -132,6 +147,8 @@ MUTATIONS = {
     "silu/sign": ("silu", _silu_wrong_sign),
     "ffn_hidden_dim/no-2/3": ("ffn_hidden_dim", _ffn_dim_no_two_thirds),
     "softmax/biased-denominator": ("softmax", _softmax_no_max),
+    "document_mask/same-id-across-documents": ("document_mask", _docmask_same_id),
+    "document_mask/no-diagonal": ("document_mask", _docmask_strict_diagonal),
 }
 
 

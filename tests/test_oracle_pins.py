@@ -371,3 +371,57 @@ def test_prefill_is_causal():
     h2 = L.prefill(ids2, lambda r: emb[r], lambda l: layers[l], norm_w, w_out, a, all_hidden=True)["hidden"]
     assert np.array_equal(h1[0, :4], h2[0, :4])
     assert not np.allclose(h1[0, 4:], h2[0, 4:])
+
+
+# ---------------------------------------------------------------------------
+# Document-level attention mask [P2 appendix item 1]
+# ---------------------------------------------------------------------------
+def test_document_mask_single_document_is_causal():
+    pos = np.arange(7)
+    assert np.array_equal(L.document_mask(pos, pos, [3] * 7), L.causal_mask(pos, pos))
+
+
+def test_document_mask_runs_and_offsets():
+    # ids [5, 5, 9, 9, 9, 5]: documents {0,1}, {2,3,4}, {5} (a repeated id after
+    # another document starts a new document)
+    m = L.document_mask(np.arange(6), np.arange(6), [5, 5, 9, 9, 9, 5])
+    vis = np.isfinite(m)
+    want = np.zeros((6, 6), dtype=bool)
+    for q, k in [(0, 0), (1, 0), (1, 1), (2, 2), (3, 2), (3, 3), (4, 2), (4, 3), (4, 4), (5, 5)]:
+        want[q, k] = True
+    assert np.array_equal(vis, want)
+    # queries at later positions (chunk after a cache)
+    m2 = L.document_mask(np.array([4, 5]), np.arange(6), [5, 5, 9, 9, 9, 5])
+    assert np.array_equal(np.isfinite(m2), want[4:6])
+
+
+def test_one_token_documents_attend_to_themselves():
+    rng = np.random.default_rng(30)
+    q, k, v = _rand_qkv(rng, S=6, H=4, G=2, hd=4)
+    pos = np.arange(6)
+    o = L.attention(q, k, v, pos, pos, doc_ids=np.arange(6)).reshape(6, 4, 4)
+    for h in range(4):
+        assert np.allclose(o[:, h], v[:, h // 2], rtol=1e-13, atol=1e-13)
+
+
+def test_packed_documents_equal_separate_sequences():
+    # RoPE makes scores depend on relative positions only [P2 3.2], so under
+    # the document mask a document packed after another gives the hidden
+    # states it gives alone from position 0
+    rng = np.random.default_rng(31)
+    a = tiny_args(theta=500000.0, L_=2)
+    layers, emb, norm_w, w_out = _tiny_model(rng, a)
+    d1, d2, d3 = [3, 1, 4, 1], [5, 9, 2], [6, 5]
+    packed = np.array([d1 + d2 + d3])
+    docs = np.array([[0] * 4 + [1] * 3 + [0] * 2])  # the third document reuses id 0
+    out = L.prefill(packed, lambda r: emb[r], lambda l: layers[l], norm_w, w_out, a, all_hidden=True,
+                    doc_ids=docs)["hidden"][0]
+    off = 0
+    for d in (d1, d2, d3):
+        alone = L.prefill(np.array([d]), lambda r: emb[r], lambda l: layers[l], norm_w, w_out, a,
+                          all_hidden=True)["hidden"][0]
+        assert np.allclose(out[off:off + len(d)], alone, rtol=1e-10, atol=1e-10)
+        off += len(d)
+    # and without the mask the later documents do change
+    plain = L.prefill(packed, lambda r: emb[r], lambda l: layers[l], norm_w, w_out, a, all_hidden=True)["hidden"][0]
+    assert not np.allclose(plain[4:], out[4:])
