@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run one workload only (profiling); the JSON line then omits the other")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the packed-document prefill and the generation loop measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (reference for HBM byte counters)")
@@ -170,6 +172,49 @@ def cpu_baseline_decode(cfg, F):
             "seconds": t}
 
 
+def bench_generate(dm, cfg, M, I, R, np, torch):
+    """The generation loop at 8B shapes: 64 prompts of 96-160 tokens (seeded
+    lengths), 32 new tokens each, greedy (graph replay and eager launches) and
+    top-p sampled (T 0.6, p 0.9, the pages' defaults)."""
+    B, gen, cap = 64, 32, 256
+    lens = [int(x) for x in 96 + I.token_ids(cfg.seed, "bench_prompt_lengths", (B,), 65)]
+    P = max(lens)
+    prompt = torch.from_numpy(I.token_ids(cfg.seed, "bench_prompts", (B, P), cfg.vocab_size)).cuda()
+    ga = R.args_for(cfg, max_batch=B, max_seq=cap)
+    caches = R.kv_caches(cfg, cfg.n_layers, B, cap)
+    kvs = M.kv_array(caches)
+    tokens = torch.empty((B, cap), dtype=torch.int32, device="cuda")
+    out_len = torch.empty((B,), dtype=torch.int32, device="cuda")
+    ws = torch.empty(M.llama_generate_workspace_bytes(ga, B, P), dtype=torch.uint8, device="cuda")
+    u = torch.from_numpy(I.uniform(cfg.seed, "bench_uniforms", (gen, B))).cuda()
+    stream = torch.cuda.Stream()
+    res = {"batch": B, "prompt_tokens": sum(lens), "new_tokens_per_seq": gen}
+
+    def run(temp, flags):
+        with torch.cuda.stream(stream):
+            M.llama_generate(ga, dm.struct, prompt, P, lens, B, gen, -1, temp, 0.9, u if temp > 0 else None, kvs,
+                             tokens, out_len, flags, ws, stream)
+        stream.synchronize()
+
+    for name, temp, flags in (("greedy_graph", 0.0, 0), ("greedy_eager", 0.0, M.LLAMA_GEN_NO_GRAPH),
+                              ("top_p_graph", 0.6, 0)):
+        run(temp, flags)  # warm-up
+        t0 = time.perf_counter()
+        run(temp, flags)
+        ms = (time.perf_counter() - t0) * 1e3
+        res[name] = {"ms": round(ms, 2), "generated_tokens_per_s": round(B * gen / (ms / 1e3), 1)}
+        log(f"generate {name}: {ms:.1f} ms for {B} x {gen} new tokens after {sum(lens)} prompt tokens")
+    # the decode phase alone: one more greedy run with per-kernel timing (eager)
+    M.llama_timing_enable(True)
+    run(0.0, M.LLAMA_GEN_NO_GRAPH)
+    rep = M.llama_timing_report()
+    M.llama_timing_enable(False)
+    res["kernel_ms_total"] = round(sum(ms for _, ms in rep.values()), 2)
+    del caches, kvs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -239,6 +284,24 @@ def main():
                                         "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                                         "traffic": measured_traffic("gemm_w1w3_swiglu"),
                                         "flop_per_launch": flop, "avg_launch_ms": dk["avg_ms"]})
+        if not args.no_extras:
+            # the same prefill over packed documents (document-level mask)
+            docs = I.document_ids(c4.seed, "bench_documents", B, S, 2048)
+            dd = torch.from_numpy(docs).cuda()
+
+            def prefill_docs():
+                M.llama_prefill_docs(pa, dm.struct, ids, dd, B, S, kv=None, logits=logits, next_id=nid, ws=ws)
+
+            dms = time_steps(prefill_docs, max(2, args.steps // 2), 1, torch)
+            dkt = kernel_times(prefill_docs, 2, M, torch)
+            lens = np.bincount(docs[0])
+            out["prefill_docs"] = {"ms_per_step": round(dms, 4), "tokens_per_s": round(B * S / (dms / 1e3), 1),
+                                   "documents": int(len(lens)), "mean_doc_len": round(float(lens.mean()), 1),
+                                   "attn_prefill_avg_ms": round(dkt["attn_prefill"]["avg_ms"], 5),
+                                   "attn_prefill_causal_avg_ms": round(kt["attn_prefill"]["avg_ms"], 5)}
+            log(f"prefill, packed documents: {dms:.3f} ms/step, attention {dkt['attn_prefill']['avg_ms']:.4f} ms "
+                f"(causal {kt['attn_prefill']['avg_ms']:.4f} ms), {len(lens)} documents")
+            del dd
         del ws, logits, ids
         torch.cuda.empty_cache()
 
@@ -288,6 +351,9 @@ def main():
         del caches, kvs, ws
         torch.cuda.empty_cache()
 
+        if not args.no_extras:
+            out["generate"] = bench_generate(dm, c5, M, I, R, np, torch)
+
     cpu = {}
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on bounded samples (cpu_baseline) ...")
@@ -332,6 +398,9 @@ def main():
         if head == "prefill" and "decode" in cpu:
             res["decode"]["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                              for k, v in cpu["decode"].items() if k != "seconds"}
+    for extra in ("prefill_docs", "generate"):
+        if extra in out:
+            res[extra] = out[extra]
     res["kernels_avg_ms"] = {w: summarize(k) for w, k in kern.items()}
     print(json.dumps(res), flush=True)
 

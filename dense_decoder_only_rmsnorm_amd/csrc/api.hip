@@ -215,6 +215,7 @@ PrefillWs carve_prefill(Carver &c, const Dims &d, int B, int S) {
 }
 
 struct HeadWs {
+  float *last;     // [M][D] fp32: gathered last rows (ragged prompts)
   u16 *hf;
   float *hf32;
   float *logits;
@@ -225,6 +226,7 @@ struct HeadWs {
 
 HeadWs carve_head(Carver &c, const Dims &d, int M) {
   HeadWs w{};
+  w.last = c.take<float>((size_t)M * d.D);
   if (d.dt == LLAMA_BF16) {
     w.hf = c.take<u16>((size_t)2 * M * d.D);
     w.nblk = skinny_nblk(d.V, SK_LOGITS);
@@ -525,16 +527,10 @@ int gen_rows_per_call(int L, int B) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(B, kGenPrefillTokens / L));
 }
 
-// Largest prefill or decode workspace any call inside generation can need.
+// Prefill (prompts padded to Lmax, gen_rows_per_call rows at a time) or
+// decode workspace, whichever is larger.
 size_t gen_inner_bytes(const Dims &d, int B, int Lmax, int cap) {
-  size_t need = decode_bytes(d, B, cap);
-  for (int g = 1; g <= B; ++g) {
-    // the longest prompt length prefilled g at a time
-    const int64_t L = g == 1 ? Lmax : std::min<int64_t>(Lmax, kGenPrefillTokens / g);
-    if (L < 1) break;
-    need = std::max(need, prefill_bytes(d, gen_rows_per_call((int)L, B), (int)L));
-  }
-  return need;
+  return std::max(decode_bytes(d, B, cap), prefill_bytes(d, gen_rows_per_call(Lmax, B), Lmax));
 }
 
 GenWs carve_gen(Carver &c, const Dims &d, int B, int Lmax, int cap) {
@@ -551,6 +547,75 @@ GenWs carve_gen(Carver &c, const Dims &d, int B, int Lmax, int cap) {
   w.rest_bytes = gen_inner_bytes(d, B, Lmax, cap);
   w.rest = c.take<char>(w.rest_bytes);
   return w;
+}
+
+
+// Prefill of `batch` sequences; with last_rows (HOST, batch <= 64) the logits
+// of sequence b come from its row last_rows[b] instead of seq_len - 1.
+int prefill_impl(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *doc_ids,
+                 int batch, int seq_len, const llama_kv *kv, float *hidden, float *logits, int32_t *next_id,
+                 const int32_t *last_rows, void *ws, size_t ws_bytes, void *stream) {
+  Dims d;
+  if (int e = check_model(a, d)) return e;
+  if (!w || !w->tok_embeddings || !w->norm || !w->output || (d.L > 0 && !w->layers))
+    return fail(LLAMA_ERR_ARG, "model weight pointer is NULL");
+  for (int l = 0; l < d.L; ++l)
+    if (int e = check_layer_w(&w->layers[l])) return e;
+  if (!ids || !next_id || !ws) return fail(LLAMA_ERR_ARG, "ids, next_id or ws is NULL");
+  if (batch < 1 || seq_len < 1) return fail(LLAMA_ERR_ARG, "batch and seq_len must be >= 1");
+  if (batch > kSkinnyRows * 1024) return fail(LLAMA_ERR_UNSUPPORTED, "batch %d too large", batch);
+  if (kv) {
+    for (int l = 0; l < d.L; ++l)
+      if (!kv[l].k || !kv[l].v) return fail(LLAMA_ERR_ARG, "kv[%d] has a NULL pointer", l);
+    if (batch > a->max_batch_size) return fail(LLAMA_ERR_SHAPE, "batch %d > max_batch_size %d", batch, a->max_batch_size);
+    if (seq_len > a->max_seq_len) return fail(LLAMA_ERR_SHAPE, "seq_len %d > max_seq_len %d", seq_len, a->max_seq_len);
+  }
+  if (last_rows) {
+    if (batch > kGenMaxBatch) return fail(LLAMA_ERR_UNSUPPORTED, "ragged batch %d above %d", batch, kGenMaxBatch);
+    for (int b = 0; b < batch; ++b)
+      if (last_rows[b] < 0 || last_rows[b] >= seq_len) return fail(LLAMA_ERR_ARG, "last row %d out of range", b);
+  }
+  const size_t need = prefill_bytes(d, batch, seq_len);
+  if (ws_bytes < need) return fail(LLAMA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((uintptr_t)ws % 256) return fail(LLAMA_ERR_ARG, "workspace not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  PrefillWs pw = carve_prefill(c, d, batch, seq_len);
+  HeadWs hw = carve_head(c, d, batch);
+  float *h = hidden ? hidden : pw.h;
+  const int T = batch * seq_len;
+  // a1: embedding rows
+  LAUNCH("embed", launch_embed(d.dt, ids, w->tok_embeddings, h, T, d.D, d.V, s));
+  LAUNCH("rope_table", launch_rope_table(pw.tab, nullptr, 0, INT32_MAX, seq_len, d.hd, a->rope_theta, s));
+  if (doc_ids) LAUNCH("doc_starts", launch_doc_starts(doc_ids, batch, 0, seq_len, pw.kv_lo, s));
+  // a2-a11: layers
+  for (int l = 0; l < d.L; ++l) {
+    if (int e = run_layer_prefill(a, d, &w->layers[l], h, h, batch, seq_len, 0, kv ? &kv[l] : nullptr, pw, true,
+                                  doc_ids ? pw.kv_lo : nullptr, s))
+      return e;
+  }
+  // a12: final norm of each sequence's last row -> hi/lo (bf16) or fp32
+  float *hl = h;
+  int64_t l_off = (int64_t)(seq_len - 1) * d.D, l_stride = (int64_t)seq_len * d.D;
+  if (last_rows) {
+    // ragged prompts padded to seq_len: gather each sequence's own last row
+    RowList rl{};
+    for (int b = 0; b < batch; ++b) rl.r[b] = b * seq_len + last_rows[b];
+    LAUNCH("gather_rows", launch_gather_rows(h, d.D, rl, batch, hw.last, s));
+    hl = hw.last;
+    l_off = 0;
+    l_stride = d.D;
+  }
+  if (d.dt == LLAMA_BF16) {
+    if (int e = rmsnorm(d, 2, hl, l_off, l_stride, nullptr, 0, 0, w->norm, a->norm_eps, hw.hf, (int64_t)batch * d.D,
+                        batch, s))
+      return e;
+  } else {
+    if (int e = rmsnorm(d, 0, hl, l_off, l_stride, nullptr, 0, 0, w->norm, a->norm_eps, hw.hf32, 0, batch, s))
+      return e;
+  }
+  // a13-a14: LM head + argmax
+  return run_head(d, hw, w->output, batch, logits, next_id, s);
 }
 
 }  // namespace
@@ -613,53 +678,9 @@ int llama_prefill(const llama_args *a, const llama_model_w *w, const int32_t *id
 int llama_prefill_docs(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *doc_ids,
                        int32_t batch, int32_t seq_len, const llama_kv *kv, float *hidden, float *logits,
                        int32_t *next_id, void *ws, size_t ws_bytes, void *stream) {
-  Dims d;
-  if (int e = check_model(a, d)) return e;
-  if (!w || !w->tok_embeddings || !w->norm || !w->output || (d.L > 0 && !w->layers))
-    return fail(LLAMA_ERR_ARG, "model weight pointer is NULL");
-  for (int l = 0; l < d.L; ++l)
-    if (int e = check_layer_w(&w->layers[l])) return e;
-  if (!ids || !next_id || !ws) return fail(LLAMA_ERR_ARG, "ids, next_id or ws is NULL");
-  if (batch < 1 || seq_len < 1) return fail(LLAMA_ERR_ARG, "batch and seq_len must be >= 1");
-  if (batch > kSkinnyRows * 1024) return fail(LLAMA_ERR_UNSUPPORTED, "batch %d too large", batch);
-  if (kv) {
-    for (int l = 0; l < d.L; ++l)
-      if (!kv[l].k || !kv[l].v) return fail(LLAMA_ERR_ARG, "kv[%d] has a NULL pointer", l);
-    if (batch > a->max_batch_size) return fail(LLAMA_ERR_SHAPE, "batch %d > max_batch_size %d", batch, a->max_batch_size);
-    if (seq_len > a->max_seq_len) return fail(LLAMA_ERR_SHAPE, "seq_len %d > max_seq_len %d", seq_len, a->max_seq_len);
-  }
-  const size_t need = prefill_bytes(d, batch, seq_len);
-  if (ws_bytes < need) return fail(LLAMA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-  if ((uintptr_t)ws % 256) return fail(LLAMA_ERR_ARG, "workspace not 256-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  Carver c(ws);
-  PrefillWs pw = carve_prefill(c, d, batch, seq_len);
-  HeadWs hw = carve_head(c, d, batch);
-  float *h = hidden ? hidden : pw.h;
-  const int T = batch * seq_len;
-  // a1: embedding rows
-  LAUNCH("embed", launch_embed(d.dt, ids, w->tok_embeddings, h, T, d.D, d.V, s));
-  LAUNCH("rope_table", launch_rope_table(pw.tab, nullptr, 0, INT32_MAX, seq_len, d.hd, a->rope_theta, s));
-  if (doc_ids) LAUNCH("doc_starts", launch_doc_starts(doc_ids, batch, 0, seq_len, pw.kv_lo, s));
-  // a2-a11: layers
-  for (int l = 0; l < d.L; ++l) {
-    if (int e = run_layer_prefill(a, d, &w->layers[l], h, h, batch, seq_len, 0, kv ? &kv[l] : nullptr, pw, true,
-                                  doc_ids ? pw.kv_lo : nullptr, s))
-      return e;
-  }
-  // a12: final norm of each sequence's last row -> hi/lo (bf16) or fp32
-  if (d.dt == LLAMA_BF16) {
-    if (int e = rmsnorm(d, 2, h, (int64_t)(seq_len - 1) * d.D, (int64_t)seq_len * d.D, nullptr, 0, 0, w->norm,
-                        a->norm_eps, hw.hf, (int64_t)batch * d.D, batch, s))
-      return e;
-  } else {
-    if (int e = rmsnorm(d, 0, h, (int64_t)(seq_len - 1) * d.D, (int64_t)seq_len * d.D, nullptr, 0, 0, w->norm,
-                        a->norm_eps, hw.hf32, 0, batch, s))
-      return e;
-  }
-  // a13-a14: LM head + argmax
-  return run_head(d, hw, w->output, batch, logits, next_id, s);
+  return prefill_impl(a, w, ids, doc_ids, batch, seq_len, kv, hidden, logits, next_id, nullptr, ws, ws_bytes, stream);
 }
+
 
 int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *pos,
                       int32_t batch, const llama_kv *kv, float *logits, int32_t *next_id, void *ws, size_t ws_bytes,
@@ -950,26 +971,27 @@ int llama_generate(const llama_args *a, const llama_model_w *w, const int32_t *p
   LAUNCH("gen_fill", launch_gen_fill(prompt, prompt_stride, tokens, cap, lens, B, s));
   int32_t ran = 0;
   if (any) {
-    // prompts: consecutive sequences of equal length share a prefill call
+    // prompts: right-padded to the longest and prefilled together (at most
+    // kGenPrefillTokens tokens per call); each sequence's first token comes
+    // from its own last prompt row.  Padded positions repeat the prompt's
+    // last token; no prompt row attends to them, and the decode step at
+    // position p writes cache slot p before any later step reads it.
     std::vector<llama_kv> kvg(std::max(d.L, 1));
-    for (int b0 = 0; b0 < B;) {
-      const int L = lens.L[b0];
-      const int gmax = gen_rows_per_call(L, B);
-      int b1 = b0 + 1;
-      while (b1 < B && lens.L[b1] == L && b1 - b0 < gmax) ++b1;
-      const int g = b1 - b0;
-      HIPCHK(hipMemcpy2DAsync(gw.ids, (size_t)L * 4, prompt + (int64_t)b0 * prompt_stride, (size_t)prompt_stride * 4,
-                              (size_t)L * 4, g, hipMemcpyDeviceToDevice, s));
-      const size_t row_bytes = (size_t)cap * d.Hk() * d.esz;
+    const int gmax = gen_rows_per_call(Lmax, B);
+    const size_t row_bytes = (size_t)cap * d.Hk() * d.esz;
+    for (int b0 = 0; b0 < B; b0 += gmax) {
+      const int g = std::min(gmax, B - b0);
+      LAUNCH("gen_stage_ids", launch_gen_stage_ids(prompt, prompt_stride, lens, b0, g, Lmax, gw.ids, s));
       for (int l = 0; l < d.L; ++l) {
         kvg[l].k = static_cast<char *>(kv[l].k) + (size_t)b0 * row_bytes;
         kvg[l].v = static_cast<char *>(kv[l].v) + (size_t)b0 * row_bytes;
       }
-      if (int e = llama_prefill(a, w, gw.ids, g, L, d.L > 0 ? kvg.data() : nullptr, nullptr,
-                                samp ? gw.logits + (int64_t)b0 * d.V : nullptr, gw.st.next + b0, gw.rest,
-                                gw.rest_bytes, stream))
+      int32_t last[kGenMaxBatch];
+      for (int i = 0; i < g; ++i) last[i] = lens.L[b0 + i] - 1;
+      if (int e = prefill_impl(a, w, gw.ids, nullptr, g, Lmax, d.L > 0 ? kvg.data() : nullptr, nullptr,
+                               samp ? gw.logits + (int64_t)b0 * d.V : nullptr, gw.st.next + b0, last, gw.rest,
+                               gw.rest_bytes, stream))
         return e;
-      b0 = b1;
     }
     if (samp)
       LAUNCH("sample_top_p", launch_sample_top_p(gw.logits, d.V, B, d.V, temperature, top_p, uniforms,

@@ -86,6 +86,28 @@ __global__ __launch_bounds__(64) void gen_step_kernel(GenState st, GenLens lens,
   if (b == 0) st.active[0] = __popcll(m);
 }
 
+// Prompt rows for one padded prefill: ids[i][j] = prompt[b0 + i][j] for
+// j < L, else the prompt's last token (the padded positions are never
+// attended to by the prompt's own rows and are overwritten by decode
+// before they are read).  Grid (ceil(S/256), g).
+__global__ __launch_bounds__(256) void gen_stage_ids_kernel(const int32_t *__restrict__ prompt, int64_t pstride,
+                                                            GenLens lens, int b0, int S, int32_t *__restrict__ ids) {
+  const int i = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= S) return;
+  const int L = lens.L[b0 + i];
+  ids[(int64_t)i * S + j] = prompt[(int64_t)(b0 + i) * pstride + min(j, L - 1)];
+}
+
+// out[i][:] = h[rows.r[i]][:] (D floats).  Grid n.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const float *__restrict__ h, int D, RowList rows,
+                                                          float *__restrict__ out) {
+  const int i = blockIdx.x;
+  const float4 *src = reinterpret_cast<const float4 *>(h + (int64_t)rows.r[i] * D);
+  float4 *dst = reinterpret_cast<float4 *>(out + (int64_t)i * D);
+  for (int c = threadIdx.x; c < D / 4; c += 256) dst[c] = src[c];
+}
+
 // out_len[b] = index of the first end-of-text token in tokens[b][0, end[b]),
 // else end[b] (the output is cut at the first end-of-text token).  Grid B.
 __global__ __launch_bounds__(256) void gen_finish_kernel(GenState st, int eos, const int32_t *__restrict__ tokens,
@@ -313,6 +335,17 @@ hipError_t launch_gen_fill(const int32_t *prompt, int64_t pstride, int32_t *toke
                            const GenLens &lens, int B, hipStream_t s) {
   hipLaunchKernelGGL(gen_fill_kernel, dim3((unsigned)((tstride + 255) / 256), B), dim3(256), 0, s, prompt, pstride,
                      tokens, tstride, lens);
+  return hipGetLastError();
+}
+
+hipError_t launch_gen_stage_ids(const int32_t *prompt, int64_t pstride, const GenLens &lens, int b0, int g, int S,
+                                int32_t *ids, hipStream_t s) {
+  hipLaunchKernelGGL(gen_stage_ids_kernel, dim3((S + 255) / 256, g), dim3(256), 0, s, prompt, pstride, lens, b0, S, ids);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const float *h, int D, const RowList &rows, int n, float *out, hipStream_t s) {
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(n), dim3(256), 0, s, h, D, rows, out);
   return hipGetLastError();
 }
 

@@ -108,6 +108,9 @@ struct GenLens {
   int32_t L[kGenMaxBatch];      // prompt length
   int32_t total[kGenMaxBatch];  // min(prompt + max_gen, max_seq_len)
 };
+struct RowList {                // row indices passed by value
+  int32_t r[kGenMaxBatch];
+};
 struct GenState {              // each [B] int32 in device memory
   int32_t *cur, *pos;          // token and position the next decode step feeds
   int32_t *done, *end;         // finished flag; one past the last written position
@@ -128,6 +131,10 @@ hipError_t launch_argmax_partial(const float *x, int rows, int n, int chunk, flo
 
 hipError_t launch_gen_fill(const int32_t *prompt, int64_t pstride, int32_t *tokens, int64_t tstride,
                            const GenLens &lens, int B, hipStream_t s);
+hipError_t launch_gen_stage_ids(const int32_t *prompt, int64_t pstride, const GenLens &lens, int b0, int g, int S,
+                                int32_t *ids, hipStream_t s);
+// D must be a multiple of 4
+hipError_t launch_gather_rows(const float *h, int D, const RowList &rows, int n, float *out, hipStream_t s);
 hipError_t launch_gen_step(const GenState &st, const GenLens &lens, int B, int eos, const int32_t *prompt,
                            int64_t pstride, int32_t *tokens, int64_t tstride, int first, hipStream_t s);
 hipError_t launch_gen_finish(const GenState &st, int B, int eos, const int32_t *tokens, int64_t tstride,

@@ -236,10 +236,11 @@ size_t llama_generate_workspace_bytes(const llama_args *a, int32_t batch, int32_
  *               instead of replaying a captured HIP graph (graphs also need
  *               a stream other than the null stream)
  *   steps_run   HOST (nullable): decode steps run
- * Prompts of equal length are prefilled together (at most 16384 tokens per
- * call); then every decode step advances all sequences at once, each at its
- * own position; a finished sequence keeps its position and its output no
- * longer changes.  The host waits on the stream every 8 steps and stops once
+ * The prompts are right-padded to the longest one and prefilled together
+ * (at most 16384 tokens per call), each sequence's first token taken from its
+ * own last prompt row; then every decode step advances all sequences at
+ * once, each at its own position; a finished sequence keeps its position and
+ * its output no longer changes.  The host waits on the stream every 8 steps and stops once
  * every sequence has finished.
  * Errors: ERR_ARG (null pointers, prompt_len out of range, max_gen_len < 0,
  *   temperature < 0, temperature > 0 without uniforms, prompt_stride <
