@@ -172,6 +172,31 @@ def cpu_baseline_decode(cfg, F):
             "seconds": t}
 
 
+def bench_long_layer(dm, cfg, M, I, R, torch):
+    """One 8B-shaped layer prefilled over 32768 positions (causal): layer time
+    and the attention kernel's rate on its unmasked pairs."""
+    S = 32768
+    lc = cfg.with_(key="long_layer", n_layers=1, seq_len=S)
+    la = R.args_for(lc, max_batch=1, max_seq=S)
+    x = torch.randn((1, S, cfg.dim), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    ws = R.workspace(la, 1, S)
+
+    def layer():
+        M.llama_layer_forward(la, dm.layers[0], x, y, 1, S, 0, kv=None, ws=ws)
+
+    ms = time_steps(layer, 3, 1, torch)
+    kt = kernel_times(layer, 2, M, torch)
+    attn_ms = kt["attn_prefill"]["avg_ms"]
+    attn_flop = 4.0 * cfg.head_dim * cfg.n_heads * (S * (S + 1) / 2)
+    res = {"seq_len": S, "layer_ms": round(ms, 3), "attn_prefill_ms": round(attn_ms, 3),
+           "attn_tflops": round(attn_flop / (attn_ms / 1e3) / 1e12, 1)}
+    log(f"one layer at S={S}: {ms:.2f} ms, attention {attn_ms:.2f} ms ({res['attn_tflops']} TFLOP/s)")
+    del x, y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_generate(dm, cfg, M, I, R, np, torch):
     """The generation loop at 8B shapes: 64 prompts of 96-160 tokens (seeded
     lengths), 32 new tokens each, greedy (graph replay and eager launches) and
@@ -304,6 +329,8 @@ def main():
             del dd
         del ws, logits, ids
         torch.cuda.empty_cache()
+        if not args.no_extras:
+            out["long_context"] = bench_long_layer(dm, c4, M, I, R, torch)
 
     if args.only in (None, "decode"):
         B, P, cap = c5.batch, c5.cache_len, c5.cache_cap
@@ -398,7 +425,7 @@ def main():
         if head == "prefill" and "decode" in cpu:
             res["decode"]["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                              for k, v in cpu["decode"].items() if k != "seconds"}
-    for extra in ("prefill_docs", "generate"):
+    for extra in ("prefill_docs", "long_context", "generate"):
         if extra in out:
             res[extra] = out[extra]
     res["kernels_avg_ms"] = {w: summarize(k) for w, k in kern.items()}
