@@ -975,20 +975,26 @@ __global__ __launch_bounds__(((HD + 63) / 64) * 64) void attn_combine_kernel(Dec
     ms = dot * a.scale * kLog2e;
     vself = a.vnew[kv];
   }
-  // The chunk partials are merged 16 at a time: each group's loads (clamped
-  // to a valid chunk; the extra ones are skipped) are issued together, and
-  // the running maximum M rescales what earlier groups summed.
+  // Only chunks that hold visible keys are merged: keys 0..pos-1 when the
+  // own term is added here, 0..pos otherwise (the chunk kernels leave the
+  // others empty).  They are merged 16 at a time: each group's loads
+  // (clamped to a valid chunk; the extra ones are skipped) are issued
+  // together, and the running maximum M rescales what earlier groups summed.
   float M = ms, L = 0.f, acc = 0.f;
   if (a.knew) {
     L = 1.f;
     acc = vself;
   }
+  int pb = a.pos[b];
+  pb = pb < 0 ? 0 : (pb > a.cap - 1 ? a.cap - 1 : pb);
+  const int nkeys = a.knew ? pb : pb + 1;
+  const int nc = min(a.nchunk, (nkeys + a.chunk - 1) / a.chunk);
   constexpr int CG = 16;
-  for (int c0 = 0; c0 < a.nchunk; c0 += CG) {
+  for (int c0 = 0; c0 < nc; c0 += CG) {
     float pm[CG], pl[CG], po[CG];
 #pragma unroll
     for (int u = 0; u < CG; ++u) {
-      const int64_t c = base + min(c0 + u, a.nchunk - 1);
+      const int64_t c = base + min(c0 + u, nc - 1);
       pm[u] = a.pm[c];
       pl[u] = a.pl[c];
       po[u] = a.po[c * HD + d];
@@ -996,7 +1002,7 @@ __global__ __launch_bounds__(((HD + 63) / 64) * 64) void attn_combine_kernel(Dec
     float Mg = M;
 #pragma unroll
     for (int u = 0; u < CG; ++u)
-      if (c0 + u < a.nchunk) Mg = fmaxf(Mg, pm[u]);
+      if (c0 + u < nc) Mg = fmaxf(Mg, pm[u]);
     if (Mg == -INFINITY) continue;  // nothing visible yet
     const float r = exp2f(M - Mg);  // 0 when M is -inf
     L *= r;
@@ -1004,7 +1010,7 @@ __global__ __launch_bounds__(((HD + 63) / 64) * 64) void attn_combine_kernel(Dec
     M = Mg;
 #pragma unroll
     for (int u = 0; u < CG; ++u) {
-      if (c0 + u >= a.nchunk || pm[u] == -INFINITY) continue;
+      if (c0 + u >= nc || pm[u] == -INFINITY) continue;
       const float w = exp2f(pm[u] - M);
       L += w * pl[u];
       acc += w * po[u];

@@ -168,6 +168,8 @@ __global__ __launch_bounds__(kSampThreads) void sample_top_p_kernel(const float 
   __shared__ uint32_t sel_digit;
   __shared__ uint64_t scan_s[kSampWaves];
   __shared__ uint32_t scan_n[kSampWaves];
+  __shared__ int picked;
+  if (tid == 0) picked = 0;
 
   // max
   float mx = -INFINITY;
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_top_p_kernel(const float 
 
   auto zkey = [&](int i, uint64_t &q) -> uint32_t {
     const float z = exp2f((x[i] - mx) * k2);
-    q = (uint64_t)(z * kFix);
+    q = (z > 0.f && z <= 1.f) ? (uint64_t)(z * kFix) : 0ull;  // NaN (non-finite logits) carries no mass
     return __float_as_uint(z);
   };
 
@@ -328,6 +330,24 @@ __global__ __launch_bounds__(kSampThreads) void sample_top_p_kernel(const float 
       if (acc > target) { pick = i; break; }
     }
     out[r] = pick;
+    picked = 1;
+  }
+  // only non-finite logits leave the target outside every kept range: fall
+  // back to the first maximum (or 0) so the output is always a valid id
+  __syncthreads();
+  if (!picked) {
+    int first = V;
+    for (int i = tid; i < V; i += kSampThreads)
+      if (x[i] == mx) { first = i; break; }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) first = min(first, __shfl_xor(first, o, kWave));
+    if (lane == 0) scan_n[wv] = (uint32_t)first;
+    __syncthreads();
+    if (tid == 0) {
+      int f = V;
+      for (int w = 0; w < kSampWaves; ++w) f = min(f, (int)scan_n[w]);
+      out[r] = f < V ? f : 0;
+    }
   }
 }
 

@@ -254,3 +254,23 @@ def test_sampler_matches_oracle(case):
     # flat distributions put most rows near a boundary; the choices still agree
     assert decided >= max(1, rows // 8)
     assert agree >= 0.9 * rows
+
+
+def test_sampler_nonfinite_logits_give_valid_ids():
+    # the sampler's contract asks for finite logits; with +inf or NaN it must
+    # still return an id inside the vocabulary (the first maximum when one exists)
+    V, rows = 5000, 4
+    lg = I.normal(12, "sampler_logits_nonfinite", (rows, V), 1.0, bf16=False).astype(np.float32)
+    lg[0, 1234] = np.inf
+    lg[1, :] = np.nan
+    lg[2, 77] = np.inf
+    lg[2, 3000] = np.inf
+    u = np.full((rows,), 0.5, dtype=np.float32)
+    out = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+    M.llama_sample_top_p(torch.from_numpy(lg).cuda(), rows, V, 0.6, 0.9, torch.from_numpy(u).cuda(), out)
+    got = out.cpu().numpy()
+    say(f"  ids {got.tolist()}")
+    assert np.all((got >= 0) & (got < V))
+    assert got[0] == 1234 and got[2] == 77
+    tok, margin = OL.sample_top_p(lg[3].astype(np.float64), 0.6, 0.9, 0.5)
+    assert got[3] == tok or margin < SAMPLE_MARGIN
