@@ -6,7 +6,7 @@ called through its C ABI (``include/llama_mi355x.h``).  PyTorch supplies
 device memory and streams.  The entry points keep the C names:
 ``llama_layer_forward``, ``llama_prefill``, ``llama_decode_step``,
 ``lm_head_argmax``, ``llama_sample_top_p``, ``llama_generate``,
-``llama_layer_forward_docs``, ``llama_prefill_docs``, plus
+``llama_layer_forward_docs``, ``llama_prefill_docs``, ``llama_decode_step_docs``, plus
 ``llama_ffn_hidden_dim``, ``llama_workspace_bytes`` and
 ``llama_generate_workspace_bytes``.
 
@@ -28,7 +28,8 @@ ERROR_NAMES = {-1: "LLAMA_ERR_ARG", -2: "LLAMA_ERR_SHAPE", -3: "LLAMA_ERR_UNSUPP
                -5: "LLAMA_ERR_HIP"}
 EXPORTED = ("llama_ffn_hidden_dim", "llama_workspace_bytes", "llama_layer_forward", "llama_prefill",
             "llama_decode_step", "lm_head_argmax", "llama_sample_top_p", "llama_generate_workspace_bytes",
-            "llama_generate", "llama_layer_forward_docs", "llama_prefill_docs", "llama_last_error",
+            "llama_generate", "llama_layer_forward_docs", "llama_prefill_docs", "llama_decode_step_docs",
+            "llama_last_error",
             "llama_timing_enable", "llama_timing_report")
 LLAMA_GEN_NO_GRAPH = 1
 
@@ -95,6 +96,9 @@ def lib() -> ctypes.CDLL:
         L.llama_prefill_docs.argtypes = [A, ctypes.POINTER(llama_model_w), vp, vp, i32, i32, ctypes.POINTER(llama_kv),
                                          vp, vp, vp, vp, sz, vp]
         L.llama_prefill_docs.restype = ctypes.c_int
+        L.llama_decode_step_docs.argtypes = [A, ctypes.POINTER(llama_model_w), vp, vp, vp, i32,
+                                             ctypes.POINTER(llama_kv), vp, vp, vp, sz, vp]
+        L.llama_decode_step_docs.restype = ctypes.c_int
         L.llama_sample_top_p.argtypes = [vp, i32, i32, ctypes.c_float, ctypes.c_float, vp, vp, vp]
         L.llama_sample_top_p.restype = ctypes.c_int
         L.llama_generate_workspace_bytes.argtypes = [A, i32, i32]
@@ -223,6 +227,15 @@ def llama_decode_step(args: llama_args, model, ids, pos, batch: int, kv, logits=
     _check(rc)
 
 
+def llama_decode_step_docs(args: llama_args, model, ids, pos, doc_start, batch: int, kv, logits=None, next_id=None,
+                           ws=None, stream=None):
+    m = model[0]
+    rc = lib().llama_decode_step_docs(ctypes.byref(args), ctypes.byref(m), _p(ids), _p(pos), _p(doc_start), batch,
+                                      kv, _p(logits), _p(next_id), _p(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream))
+    _check(rc)
+
+
 def lm_head_argmax(args: llama_args, h, final_norm_w, w_out, M: int, logits=None, argmax=None, ws=None,
                    stream=None):
     rc = lib().lm_head_argmax(ctypes.byref(args), _p(h), _p(final_norm_w), _p(w_out), M, _p(logits), _p(argmax),
@@ -276,5 +289,5 @@ __all__ = ["llama_timing_enable", "llama_timing_report", "lib", "last_error", "L
            "make_args", "layer_struct", "model_struct", "kv_array", "llama_ffn_hidden_dim",
            "llama_workspace_bytes", "llama_layer_forward", "llama_prefill", "llama_decode_step", "lm_head_argmax",
            "llama_sample_top_p", "llama_generate_workspace_bytes", "llama_generate", "LLAMA_GEN_NO_GRAPH",
-           "llama_layer_forward_docs", "llama_prefill_docs",
+           "llama_layer_forward_docs", "llama_prefill_docs", "llama_decode_step_docs",
            "LLAMA_F32", "LLAMA_BF16", "EXPORTED"]

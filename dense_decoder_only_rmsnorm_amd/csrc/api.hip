@@ -685,6 +685,12 @@ int llama_prefill_docs(const llama_args *a, const llama_model_w *w, const int32_
 int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *pos,
                       int32_t batch, const llama_kv *kv, float *logits, int32_t *next_id, void *ws, size_t ws_bytes,
                       void *stream) {
+  return llama_decode_step_docs(a, w, ids, pos, nullptr, batch, kv, logits, next_id, ws, ws_bytes, stream);
+}
+
+int llama_decode_step_docs(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *pos,
+                           const int32_t *doc_start, int32_t batch, const llama_kv *kv, float *logits,
+                           int32_t *next_id, void *ws, size_t ws_bytes, void *stream) {
   Dims d;
   if (int e = check_model(a, d)) return e;
   if (!w || !w->tok_embeddings || !w->norm || !w->output || (d.L > 0 && !w->layers))
@@ -796,6 +802,7 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
     da.out = dw.o;
     da.out_mode = bf ? 2 : 0;
     da.out_plane = (int64_t)B * d.Hq();
+    da.kv_lo = doc_start;
     LAUNCH("attn_decode", launch_attn_decode(d.dt, da, s));
     LAUNCH("attn_combine", launch_attn_combine(da, s));
     if (bf) {

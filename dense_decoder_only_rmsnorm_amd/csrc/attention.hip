@@ -521,8 +521,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecodeAttnArgs a) {
   const int n_rep = a.H / a.G;
   int pb = a.pos[b];
   pb = pb < 0 ? 0 : (pb > a.cap - 1 ? a.cap - 1 : pb);
-  const int c0 = ci * CH;
-  const int kend = min(c0 + CH, a.knew ? pb : pb + 1);  // own position added by the combine when knew is set
+  const int kstart = a.kv_lo ? min(max(a.kv_lo[b], 0), pb) : 0;  // lowest visible key (document)
+  const int c0 = max(ci * CH, kstart);
+  const int kend = min(ci * CH + CH, a.knew ? pb : pb + 1);  // own position added by the combine when knew is set
   const int64_t pidx = ((int64_t)b * a.H + g * n_rep) * a.nchunk + ci;  // + r * nchunk per head
   if (c0 >= kend) {
     for (int i = tid; i < n_rep * HD; i += 256) {
@@ -612,8 +613,9 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(DecodeAttnArgs a) {
   pb = pb < 0 ? 0 : (pb > a.cap - 1 ? a.cap - 1 : pb);
   const int c0 = ci * CH;
   const int kend = min(c0 + CH, a.knew ? pb : pb + 1);  // own position added by the combine when knew is set
+  const int kstart = a.kv_lo ? min(max(a.kv_lo[b], 0), pb) : 0;  // lowest visible key (document)
   const int64_t pidx = ((int64_t)b * a.H + g * n_rep) * a.nchunk + ci;
-  if (c0 >= kend) {
+  if (c0 >= kend || c0 + CH <= kstart) {
     for (int i = tid; i < n_rep * HD; i += 256) a.po[(pidx + (int64_t)(i / HD) * a.nchunk) * HD + i % HD] = 0.f;
     if (tid < n_rep) {
       a.pm[pidx + (int64_t)tid * a.nchunk] = -INFINITY;
@@ -676,7 +678,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(DecodeAttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int key = kw0 + kb * 16 + 4 * grp + r;
-      if (key >= kend) sc[kb][r] = -INFINITY;
+      if (key >= kend || key < kstart) sc[kb][r] = -INFINITY;
       mx = fmaxf(mx, sc[kb][r]);
     }
   }
@@ -797,8 +799,9 @@ __global__ __launch_bounds__(256) void attn_decode_mfma2(DecodeAttnArgs a) {
   pb = pb < 0 ? 0 : (pb > a.cap - 1 ? a.cap - 1 : pb);
   const int c0 = ci * CH;
   const int kend = min(c0 + CH, a.knew ? pb : pb + 1);  // own position added by the combine when knew is set
+  const int kstart = a.kv_lo ? min(max(a.kv_lo[b], 0), pb) : 0;  // lowest visible key (document)
   const int64_t pidx = ((int64_t)b * a.H + g * n_rep) * a.nchunk + ci;
-  if (c0 >= kend) {
+  if (c0 >= kend || c0 + CH <= kstart) {
     for (int i = tid; i < n_rep * HD; i += 256) a.po[(pidx + (int64_t)(i / HD) * a.nchunk) * HD + i % HD] = 0.f;
     if (tid < n_rep) {
       a.pm[pidx + (int64_t)tid * a.nchunk] = -INFINITY;
@@ -862,7 +865,8 @@ __global__ __launch_bounds__(256) void attn_decode_mfma2(DecodeAttnArgs a) {
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if (kw0 + kb * 16 + 4 * grp + r >= kend) sc[kb][r] = -INFINITY;
+      const int key = kw0 + kb * 16 + 4 * grp + r;
+      if (key >= kend || key < kstart) sc[kb][r] = -INFINITY;
       mx = fmaxf(mx, sc[kb][r]);
     }
   }

@@ -100,6 +100,9 @@ struct DecodeAttnArgs {
   float scale;
   float *pm; float *pl; float *po;        // partials [B][H][nchunk] (m, l), [B][H][nchunk][hd]
   void *out; int out_mode; int64_t out_plane;  // [B][H*hd]: 0 fp32, 2 bf16 hi/lo planes
+  // optional [B]: the lowest visible cache position of each sequence (the
+  // first position of its current document); keys below it get zero weight
+  const int32_t *kv_lo;
 };
 
 // Token generation: per-sequence lengths (passed by value) and device state.

@@ -178,6 +178,17 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
                       int32_t batch, const llama_kv *kv, float *logits, int32_t *next_id, void *ws,
                       size_t ws_bytes, void *stream);
 
+/* llama_decode_step with the document-level attention mask (see
+ * llama_layer_forward_docs): the new token continues the document that
+ * starts at cache position doc_start[b] and attends to positions
+ * doc_start[b]..pos[b] only.
+ *   doc_start [batch] int32 (device, nullable; NULL = llama_decode_step);
+ *     values are clamped to [0, pos[b]].
+ * Errors: as llama_decode_step. */
+int llama_decode_step_docs(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *pos,
+                           const int32_t *doc_start, int32_t batch, const llama_kv *kv, float *logits,
+                           int32_t *next_id, void *ws, size_t ws_bytes, void *stream);
+
 /* Output head on M hidden rows [P1 11-12; P3 1-4]:
  *   h [M][dim] fp32 (device); final_norm_w (nullable, dtype) applies the
  *   final RMSNorm first; w_out [vocab][dim] (dtype).

@@ -319,11 +319,13 @@ def prefill(ids, embed_rows: Callable, layer: LayerSource, norm_w, w_out, args: 
 
 
 def decode_step(ids, caches: Sequence[Sequence[dict]], embed_rows: Callable, layer: LayerSource,
-                norm_w, w_out, args: dict, new_kv: Optional[list] = None):
+                norm_w, w_out, args: dict, new_kv: Optional[list] = None, doc_ids=None):
     """One new token per sequence at position p_b = len(cache) [P2 3.3, 6 generate].
 
     ids: [B] token ids; caches[b][l] = {"k": [p_b, G, hd], "v": ...} (not modified).
     When ``new_kv`` is a list, it receives per (b, l) the new key/value rows.
+    ``doc_ids`` (optional, per sequence the ids of positions 0..p_b, the new
+    token's included) applies the document-level mask.
     """
     ids = np.asarray(ids).reshape(-1)
     B = ids.shape[0]
@@ -334,7 +336,10 @@ def decode_step(ids, caches: Sequence[Sequence[dict]], embed_rows: Callable, lay
             c = caches[b][l]
             p = c["k"].shape[0]
             cache = {"k": c["k"], "v": c["v"]}
-            hs[b] = layer_forward(hs[b], lw, args, np.array([p]), cache=cache)
+            if doc_ids is None:
+                hs[b] = layer_forward(hs[b], lw, args, np.array([p]), cache=cache)
+            else:
+                hs[b] = layer_forward(hs[b], lw, args, np.array([p]), cache=cache, doc_ids=doc_ids[b])
             if new_kv is not None:
                 new_kv.append((b, l, cache["k"][-1], cache["v"][-1]))
     last = np.stack([hs[b][-1] for b in range(B)])

@@ -1,6 +1,7 @@
 """GPU parity of the document-level attention mask [P2 appendix item 1]:
 packed documents attend only within themselves.  The HIP path (through
-llama_layer_forward_docs / llama_prefill_docs) is compared with the oracle's
+llama_layer_forward_docs / llama_prefill_docs / llama_decode_step_docs) is
+compared with the oracle's
 document_mask on seeded packed sequences (document lengths uniform in
 [1, max_doc])."""
 import numpy as np
@@ -11,6 +12,7 @@ import dense_decoder_only_rmsnorm_amd as M
 import inputs as I
 from dense_decoder_only_rmsnorm_amd import runtime as R
 from gpu_util import BF16_TOL, F32_TOL, assert_argmax, assert_close, host, say
+from oracle import llama as OL
 from oracle import runner as OR
 
 from test_gpu_parity import small_cfg
@@ -136,3 +138,44 @@ def test_8b_layer_s2048_documents_sampled_rows():
     rows = sorted(set([0, 1, 63, 64, 255, 1000, 2047] + starts[:3] + [p - 1 for p in starts[:3]] + starts[-2:]))
     ref = OR.layer(cfg, x, rows=rows, doc_ids=docs)["y"]
     assert_close(host(y)[:, rows], ref, BF16_TOL, "8B layer S=2048 documents, sampled rows")
+
+
+@pytest.mark.parametrize("dtype,D,H,G", [("bf16", 1024, 8, 2), ("bf16", 256, 4, 2), ("f32", 256, 4, 2)])
+def test_decode_after_packed_prefill(dtype, D, H, G):
+    # prefill of packed documents into the cache, then one decode step:
+    # sequences 0 and 2 continue their last document, sequence 1 starts a new one
+    S, B, cap = 300, 3, 384
+    cfg = small_cfg(dtype, D, H, G, S, B, L=2, V=3000, seed=16).with_(kind="prefill")
+    docs = I.document_ids(16, f"docs-decode-{dtype}-{D}", B, S, 120)
+    say(f"case decode after packed prefill {cfg.key}")
+    dm = R.DeviceModel(cfg)
+    args = dm.args
+    args.max_batch_size, args.max_seq_len = B, cap
+    ids = I.prompt_ids(cfg)
+    caches = R.kv_caches(cfg, cfg.n_layers, B, cap)
+    kvs = M.kv_array(caches)
+    ws = R.workspace(args, B, S)
+    nid = torch.empty(B, dtype=torch.int32, device="cuda")
+    M.llama_prefill_docs(args, dm.struct, _ids(ids), _ids(docs), B, S, kv=kvs, next_id=nid, ws=ws)
+    new_ids = np.array([5, 77, 2999], dtype=np.int32)
+    last_start = [int(S - np.argmax(docs[b][::-1] != docs[b][-1])) if np.any(docs[b] != docs[b][-1]) else 0
+                  for b in range(B)]
+    doc_start = np.array([last_start[0], S, last_start[2]], dtype=np.int32)
+    pos = torch.full((B,), S, dtype=torch.int32, device="cuda")
+    logits = torch.empty((B, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    M.llama_decode_step_docs(args, dm.struct, _ids(new_ids), pos, _ids(doc_start), B, kvs, logits=logits,
+                             next_id=nid, ws=ws)
+    torch.cuda.synchronize()
+    ocaches = [[] for _ in range(B)]
+    OR.prefill(cfg, ids, caches=ocaches, doc_ids=docs)
+    ext = [np.append(docs[b], docs[b][-1] if doc_start[b] < S else docs[b][-1] + 1) for b in range(B)]
+    m = OR.model_of(cfg)
+    ref = OL.decode_step(new_ids, ocaches, lambda r: m.rows("tok_embeddings", r), m.layer, m.get("norm"),
+                         m.get("output"), OR.args_of(cfg), doc_ids=ext)
+    tol = BF16_TOL if cfg.bf16 else F32_TOL
+    assert_close(host(logits), ref["logits"], tol, "decode logits (document mask)")
+    assert_argmax(nid.cpu().numpy(), ref["logits"], "decode argmax (document mask)")
+    # the plain causal step differs for the sequences whose document started after position 0
+    plain = OL.decode_step(new_ids, ocaches, lambda r: m.rows("tok_embeddings", r), m.layer, m.get("norm"),
+                           m.get("output"), OR.args_of(cfg))
+    assert not np.allclose(plain["logits"][1], ref["logits"][1], rtol=1e-3, atol=1e-3)
