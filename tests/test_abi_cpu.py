@@ -175,3 +175,23 @@ def test_generate_workspace_bytes():
     assert n2 >= M.llama_workspace_bytes(a, 4, 64)
     with pytest.raises(M.LlamaError):
         M.llama_generate_workspace_bytes(a, 65, 8)
+
+
+def test_document_entry_points_argument_errors():
+    a = _args()
+    L = M.lib()
+    layers = (M.llama_layer_w * 2)(_layer_fake(), _layer_fake())
+    model = M.llama_model_w(0x1000, ctypes.cast(layers, ctypes.POINTER(M.llama_layer_w)), 0x1000, 0x1000)
+    kvs = (M.llama_kv * 2)(M.llama_kv(0x1000, 0x1000), M.llama_kv(0x1000, 0x1000))
+    rc = L.llama_decode_step_docs(ctypes.byref(a), ctypes.byref(model), FAKE, None, FAKE, 2, kvs, None, FAKE, FAKE,
+                                  1 << 40, None)
+    assert rc == M.LLAMA_ERR_ARG  # pos is NULL
+    rc = L.llama_decode_step_docs(ctypes.byref(a), ctypes.byref(model), FAKE, FAKE, FAKE, 9, kvs, None, FAKE, FAKE,
+                                  1 << 40, None)
+    assert rc == M.LLAMA_ERR_SHAPE  # batch > max_batch_size
+    rc = L.llama_prefill_docs(ctypes.byref(a), ctypes.byref(model), None, FAKE, 1, 8, None, None, None, FAKE, FAKE,
+                              1 << 40, None)
+    assert rc == M.LLAMA_ERR_ARG  # ids NULL
+    rc = L.llama_layer_forward_docs(ctypes.byref(a), ctypes.byref(_layer_fake()), FAKE, FAKE, 1, 8, 3, None, FAKE,
+                                    FAKE, 1 << 40, None)
+    assert rc == M.LLAMA_ERR_ARG  # start_pos > 0 without a cache
