@@ -197,12 +197,11 @@ def bench_long_layer(dm, cfg, M, I, R, torch):
     return res
 
 
-def bench_generate(dm, cfg, M, I, R, np, torch):
-    """The generation loop at 8B shapes: 64 prompts of 96-160 tokens (seeded
-    lengths), 32 new tokens each, greedy (graph replay and eager launches) and
-    top-p sampled (T 0.6, p 0.9, the pages' defaults)."""
-    B, gen, cap = 64, 32, 256
-    lens = [int(x) for x in 96 + I.token_ids(cfg.seed, "bench_prompt_lengths", (B,), 65)]
+def bench_generate(dm, cfg, M, I, R, np, torch, B=64, gen=32, cap=256, lmin=96, lspan=65):
+    """The generation loop: B prompts of lmin .. lmin+lspan-1 tokens (seeded
+    lengths), gen new tokens each, greedy (graph replay and eager launches)
+    and top-p sampled (T 0.6, p 0.9, the pages' defaults)."""
+    lens = [int(x) for x in lmin + I.token_ids(cfg.seed, "bench_prompt_lengths", (B,), lspan)]
     P = max(lens)
     prompt = torch.from_numpy(I.token_ids(cfg.seed, "bench_prompts", (B, P), cfg.vocab_size)).cuda()
     ga = R.args_for(cfg, max_batch=B, max_seq=cap)
@@ -221,17 +220,16 @@ def bench_generate(dm, cfg, M, I, R, np, torch):
                              tokens, out_len, flags, ws, stream)
         stream.synchronize()
 
-    for name, temp, flags in (("greedy_graph", 0.0, 0), ("greedy_eager", 0.0, M.LLAMA_GEN_NO_GRAPH),
-                              ("top_p_graph", 0.6, 0)):
+    for name, temp, flags in (("greedy", 0.0, 0), ("greedy_graph", 0.0, M.LLAMA_GEN_GRAPH), ("top_p", 0.6, 0)):
         run(temp, flags)  # warm-up
         t0 = time.perf_counter()
         run(temp, flags)
         ms = (time.perf_counter() - t0) * 1e3
         res[name] = {"ms": round(ms, 2), "generated_tokens_per_s": round(B * gen / (ms / 1e3), 1)}
         log(f"generate {name}: {ms:.1f} ms for {B} x {gen} new tokens after {sum(lens)} prompt tokens")
-    # the decode phase alone: one more greedy run with per-kernel timing (eager)
+    # one more greedy run with per-kernel timing (eager launches)
     M.llama_timing_enable(True)
-    run(0.0, M.LLAMA_GEN_NO_GRAPH)
+    run(0.0, 0)
     rep = M.llama_timing_report()
     M.llama_timing_enable(False)
     res["kernel_ms_total"] = round(sum(ms for _, ms in rep.values()), 2)
@@ -380,6 +378,13 @@ def main():
 
         if not args.no_extras:
             out["generate"] = bench_generate(dm, c5, M, I, R, np, torch)
+            # the same loop on the small 4-layer GQA stack (launch-bound steps)
+            c2 = I.CONFIGS["c2"]
+            dm2 = R.DeviceModel(c2)
+            out["generate_small"] = bench_generate(dm2, c2, M, I, R, np, torch, B=4, gen=64, cap=256, lmin=16,
+                                                   lspan=17)
+            out["generate_small"]["model"] = "dim 768, 4 layers, 8 heads / 2 KV heads, vocab 32000, bf16"
+            del dm2
 
     cpu = {}
     if not args.no_cpu_baseline:
@@ -425,7 +430,7 @@ def main():
         if head == "prefill" and "decode" in cpu:
             res["decode"]["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                              for k, v in cpu["decode"].items() if k != "seconds"}
-    for extra in ("prefill_docs", "long_context", "generate"):
+    for extra in ("prefill_docs", "long_context", "generate", "generate_small"):
         if extra in out:
             res[extra] = out[extra]
     res["kernels_avg_ms"] = {w: summarize(k) for w, k in kern.items()}

@@ -31,7 +31,7 @@ EXPORTED = ("llama_ffn_hidden_dim", "llama_workspace_bytes", "llama_layer_forwar
             "llama_generate", "llama_layer_forward_docs", "llama_prefill_docs", "llama_decode_step_docs",
             "llama_last_error",
             "llama_timing_enable", "llama_timing_report")
-LLAMA_GEN_NO_GRAPH = 1
+LLAMA_GEN_GRAPH = 2
 
 
 class LlamaError(RuntimeError):
@@ -288,6 +288,6 @@ def llama_timing_report() -> dict:
 __all__ = ["llama_timing_enable", "llama_timing_report", "lib", "last_error", "LlamaError", "llama_args", "llama_layer_w", "llama_model_w", "llama_kv",
            "make_args", "layer_struct", "model_struct", "kv_array", "llama_ffn_hidden_dim",
            "llama_workspace_bytes", "llama_layer_forward", "llama_prefill", "llama_decode_step", "lm_head_argmax",
-           "llama_sample_top_p", "llama_generate_workspace_bytes", "llama_generate", "LLAMA_GEN_NO_GRAPH",
+           "llama_sample_top_p", "llama_generate_workspace_bytes", "llama_generate", "LLAMA_GEN_GRAPH",
            "llama_layer_forward_docs", "llama_prefill_docs", "llama_decode_step_docs",
            "LLAMA_F32", "LLAMA_BF16", "EXPORTED"]

@@ -1024,7 +1024,7 @@ int llama_generate(const llama_args *a, const llama_model_w *w, const int32_t *p
       std::lock_guard<std::mutex> lk(g_timing.mu);
       timing_on = g_timing.on;
     }
-    const bool use_graph = steps > 0 && !(flags & LLAMA_GEN_NO_GRAPH) && s != nullptr && !timing_on;
+    const bool use_graph = steps > 0 && (flags & LLAMA_GEN_GRAPH) && s != nullptr && !timing_on;
     hipGraphExec_t ge = nullptr;
     if (use_graph) {
       HIPCHK(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));

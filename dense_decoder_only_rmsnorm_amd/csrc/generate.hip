@@ -151,6 +151,13 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t *red) {
   return t;
 }
 
+// Radix digits of the 32-bit key, most significant first.  Bits 31..30 are
+// zero for every z in [0, 1] (sign 0, exponent at most 127), so the first
+// digit is bits 29..22: the exponent spread over ~80 buckets instead of the
+// ~20 the top byte would use, which keeps the histogram atomics apart.
+__device__ __forceinline__ int digit_shift(int pass) { return pass < 3 ? 22 - 8 * pass : 0; }
+__device__ __forceinline__ int digit_bits(int pass) { return pass < 3 ? 8 : 6; }
+
 // One block per row.  logits [M][ld] fp32; u [urows][M] (row of each logits
 // row chosen by gidx[r], clamped to urows - 1, or row 0 when gidx is null).
 __global__ __launch_bounds__(kSampThreads) void sample_top_p_kernel(const float *__restrict__ logits, int64_t ld,
@@ -159,15 +166,15 @@ __global__ __launch_bounds__(kSampThreads) void sample_top_p_kernel(const float 
                                                                     const int32_t *__restrict__ gidx,
                                                                     int32_t *__restrict__ out) {
   const int r = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float *x = logits + (int64_t)r * ld;
-  __shared__ uint64_t hist[256];
+  __shared__ uint64_t hist[kSampWaves][256];  // one histogram per wave (fewer colliding atomics)
   __shared__ uint64_t red[kSampWaves];
   __shared__ float redf[kSampWaves];
   __shared__ uint64_t sel_mass;   // mass of keys above the selected prefix
   __shared__ uint32_t sel_digit;
-  __shared__ uint64_t scan_s[kSampWaves];
-  __shared__ uint32_t scan_n[kSampWaves];
+  __shared__ uint64_t wmass[kSampWaves];
+  __shared__ uint32_t wties[kSampWaves];
   __shared__ int picked;
   if (tid == 0) picked = 0;
 
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_top_p_kernel(const float 
   float mx = -INFINITY;
   for (int i = tid; i < V; i += kSampThreads) mx = fmaxf(mx, x[i]);
   mx = wave_max(mx);
-  if ((tid & 63) == 0) redf[tid >> 6] = mx;
+  if (lane == 0) redf[wv] = mx;
   __syncthreads();
   mx = redf[0];
 #pragma unroll
@@ -186,9 +193,21 @@ __global__ __launch_bounds__(kSampThreads) void sample_top_p_kernel(const float 
     q = (z > 0.f && z <= 1.f) ? (uint64_t)(z * kFix) : 0ull;  // NaN (non-finite logits) carries no mass
     return __float_as_uint(z);
   };
+  uint64_t *hflat = &hist[0][0];
+  // merge the per-wave histograms into hist[0] (thread t owns bucket t)
+  auto merge_hist = [&]() {
+    __syncthreads();
+    if (tid < 256) {
+      uint64_t t = 0;
+#pragma unroll
+      for (int w = 0; w < kSampWaves; ++w) t += hist[w][tid];
+      hist[0][tid] = t;
+    }
+    __syncthreads();
+  };
 
-  // total mass + first histogram (key bits 31..24)
-  if (tid < 256) hist[tid] = 0;
+  // total mass + first histogram
+  for (int i = tid; i < kSampWaves * 256; i += kSampThreads) hflat[i] = 0;
   __syncthreads();
   uint64_t tot = 0;
   for (int i = tid; i < V; i += kSampThreads) {
@@ -196,7 +215,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_top_p_kernel(const float 
     const uint32_t key = zkey(i, q);
     if (q) {
       tot += q;
-      atomicAdd((unsigned long long *)&hist[key >> 24], (unsigned long long)q);
+      atomicAdd((unsigned long long *)&hist[wv][(key >> 22) & 255], (unsigned long long)q);
     }
   }
   const uint64_t Z = block_sum_u64(tot, red);
@@ -211,36 +230,34 @@ __global__ __launch_bounds__(kSampThreads) void sample_top_p_kernel(const float 
     const uint64_t R = (uint64_t)((double)top_p * (double)Z);
     uint32_t prefix = 0;
     for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
+      const int shift = digit_shift(pass), nb = 1 << digit_bits(pass);
       if (pass > 0) {
         __syncthreads();
-        if (tid < 256) hist[tid] = 0;
+        for (int i = tid; i < kSampWaves * 256; i += kSampThreads) hflat[i] = 0;
         __syncthreads();
-        const uint32_t pmask = 0xFFFFFFFFu << (shift + 8);
+        const int hi = shift + digit_bits(pass);  // bits at and above hi are fixed by the prefix
         for (int i = tid; i < V; i += kSampThreads) {
           uint64_t q;
           const uint32_t key = zkey(i, q);
-          if (q && (key & pmask) == prefix)
-            atomicAdd((unsigned long long *)&hist[(key >> shift) & 255], (unsigned long long)q);
+          if (q && (key >> hi) == (prefix >> hi))
+            atomicAdd((unsigned long long *)&hist[wv][(key >> shift) & (nb - 1)], (unsigned long long)q);
         }
       }
-      __syncthreads();
-      // wave 0: the largest digit d with above + sum(hist[d..255]) > R
+      merge_hist();
+      // wave 0: the largest digit d with above + sum(hist[d..]) > R
       if (tid < 64) {
-        uint64_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
-        const uint64_t mine = h0 + h1 + h2 + h3;
-        // suffix sum over lanes tid+1..63
+        const uint64_t h0 = hist[0][4 * tid], h1 = hist[0][4 * tid + 1], h2 = hist[0][4 * tid + 2],
+                       h3 = hist[0][4 * tid + 3];
+        const uint64_t mine = h0 + h1 + h2 + h3;  // buckets past nb are zero
         uint64_t suf = mine;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
           const uint64_t t = __shfl_down(suf, o, kWave);
           if (tid + o < 64) suf += t;
         }
-        const uint64_t after = suf - mine;  // mass of digits above this lane's four
-        uint64_t base = above + after;
+        const uint64_t base = above + (suf - mine);  // mass of the digits above this lane's four
         int d = -1;
         uint64_t dm = 0;
-        // within the lane, from the highest digit down
         if (base + h3 > R) { d = 4 * tid + 3; dm = base; }
         else if (base + h3 + h2 > R) { d = 4 * tid + 2; dm = base + h3; }
         else if (base + h3 + h2 + h1 > R) { d = 4 * tid + 1; dm = base + h3 + h2; }
@@ -263,74 +280,82 @@ __global__ __launch_bounds__(kSampThreads) void sample_top_p_kernel(const float 
     const uint64_t qs = (uint64_t)(__uint_as_float(thr) * kFix);
     take = qs ? (R - above) / qs + 1 : 0;
   }
+  const uint64_t qs = keep_all ? 0 : (uint64_t)(__uint_as_float(thr) * kFix);
 
-  // kept mass and draw target
-  // contiguous ranges of 128 ids per thread (1024 * 128 >= V is checked on the host)
-  const int i0 = tid * 128, i1 = min(V, i0 + 128);
-  uint64_t s_keep_gt = 0;  // mass of kept keys > t* in this range
-  uint32_t n_tie = 0;      // tokens with key == t* (and q > 0) in this range
-  for (int i = i0; i < i1; ++i) {
+  // kept mass and ties per wave over contiguous id ranges (coalesced, 64 ids a step)
+  const int chunk = (((V + kSampWaves - 1) / kSampWaves) + 63) & ~63;
+  const int w0 = wv * chunk, w1 = min(V, w0 + chunk);
+  uint64_t m_gt = 0;
+  uint32_t n_tie = 0;
+  for (int i = w0 + lane; i < w1; i += 64) {
     uint64_t q;
     const uint32_t key = zkey(i, q);
     if (!q) continue;
-    if (keep_all || key > thr) s_keep_gt += q;
+    if (keep_all || key > thr) m_gt += q;
     else if (key == thr) ++n_tie;
   }
-  // exclusive scans of n_tie (tie rank) and of kept mass (needs tie ranks)
-  const int lane = tid & 63, wv = tid >> 6;
-  uint32_t ninc = n_tie;
+  m_gt = wave_sum_u64(m_gt);
+  uint32_t nt = n_tie;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(ninc, o, kWave);
-    if (lane >= o) ninc += t;
+  for (int o = 32; o >= 1; o >>= 1) nt += __shfl_xor(nt, o, kWave);
+  if (lane == 0) {
+    wmass[wv] = m_gt;
+    wties[wv] = nt;
   }
-  if (lane == 63) scan_n[wv] = ninc;
   __syncthreads();
-  uint32_t nbase = 0;
-  for (int w = 0; w < wv; ++w) nbase += scan_n[w];
-  const uint32_t tie0 = nbase + ninc - n_tie;  // rank of this range's first tie
-  const uint64_t qs = keep_all ? 0 : (uint64_t)(__uint_as_float(thr) * kFix);
-  const uint32_t tie_keep = keep_all ? 0u
-                            : (uint32_t)min((uint64_t)n_tie, (take > tie0 ? take - tie0 : 0ull));
-  const uint64_t s_keep = s_keep_gt + (uint64_t)tie_keep * qs;
-  uint64_t sinc = s_keep;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint64_t t = __shfl_up(sinc, o, kWave);
-    if (lane >= o) sinc += t;
-  }
-  if (lane == 63) scan_s[wv] = sinc;
-  __syncthreads();
-  uint64_t sbase = 0, Mk = 0;
+  // per wave: ties before it (in id order), its kept mass (its ties stay
+  // while their rank is below take); prefix over the waves before this one
+  uint32_t tp = 0, tie0 = 0;
+  uint64_t pre = 0, Mk = 0, mine = 0;
   for (int w = 0; w < kSampWaves; ++w) {
-    if (w < wv) sbase += scan_s[w];
-    Mk += scan_s[w];
+    const uint64_t kt = keep_all ? 0 : min((uint64_t)wties[w], take > tp ? take - tp : 0ull);
+    const uint64_t mw = wmass[w] + kt * qs;
+    if (w < wv) pre += mw;
+    if (w == wv) {
+      tie0 = tp;
+      mine = mw;
+    }
+    Mk += mw;
+    tp += wties[w];
   }
-  const uint64_t pre = sbase + sinc - s_keep;  // kept mass before this range
 
   const int urow = gidx ? min(max(gidx[r], 0), urows - 1) : 0;
   const float uu = u[(int64_t)urow * M + r];
   uint64_t target = (uint64_t)((double)uu * (double)Mk);
-  if (target >= Mk) target = Mk - 1;
-  // the thread whose kept range [pre, pre + s_keep) holds the target walks it
-  if (s_keep && target >= pre && target < pre + s_keep) {
+  if (Mk && target >= Mk) target = Mk - 1;
+  // the wave whose kept range [pre, pre + mine) holds the target walks it in
+  // id order, 64 ids a step, with a wave-wide inclusive scan of the kept mass
+  if (mine && target >= pre && target < pre + mine) {
     uint64_t acc = pre;
     uint32_t rank = tie0;
-    int pick = i1 - 1;
-    for (int i = i0; i < i1; ++i) {
-      uint64_t q;
-      const uint32_t key = zkey(i, q);
-      if (!q) continue;
-      bool kept;
-      if (keep_all || key > thr) kept = true;
-      else if (key == thr) kept = (uint64_t)(rank++) < take;
-      else kept = false;
-      if (!kept) continue;
-      acc += q;
-      if (acc > target) { pick = i; break; }
+    for (int i0 = w0; i0 < w1; i0 += 64) {
+      const int i = i0 + lane;
+      uint64_t q = 0;
+      uint32_t key = 0;
+      if (i < w1) key = zkey(i, q);
+      const bool tie = q && !keep_all && key == thr;
+      const uint64_t tmask = __ballot(tie);
+      const uint32_t my_rank = rank + __popcll(tmask & ((1ull << lane) - 1ull));
+      bool kept = false;
+      if (q) kept = keep_all || key > thr || (tie && (uint64_t)my_rank < take);
+      uint64_t v = kept ? q : 0;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t t = __shfl_up(v, o, kWave);
+        if (lane >= o) v += t;
+      }
+      const uint64_t hitm = __ballot(kept && acc + v > target);
+      if (hitm) {
+        const int first = __ffsll((long long)hitm) - 1;
+        if (lane == first) {
+          out[r] = i;
+          picked = 1;
+        }
+        break;
+      }
+      acc += __shfl(v, 63, kWave);
+      rank += __popcll(tmask);
     }
-    out[r] = pick;
-    picked = 1;
   }
   // only non-finite logits leave the target outside every kept range: fall
   // back to the first maximum (or 0) so the output is always a valid id
@@ -341,11 +366,11 @@ __global__ __launch_bounds__(kSampThreads) void sample_top_p_kernel(const float 
       if (x[i] == mx) { first = i; break; }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) first = min(first, __shfl_xor(first, o, kWave));
-    if (lane == 0) scan_n[wv] = (uint32_t)first;
+    if (lane == 0) wties[wv] = (uint32_t)first;
     __syncthreads();
     if (tid == 0) {
       int f = V;
-      for (int w = 0; w < kSampWaves; ++w) f = min(f, (int)scan_n[w]);
+      for (int w = 0; w < kSampWaves; ++w) f = min(f, (int)wties[w]);
       out[r] = f < V ? f : 0;
     }
   }

@@ -220,7 +220,7 @@ int llama_sample_top_p(const float *logits, int32_t M, int32_t V, float temperat
  * hold at most max_prompt_len tokens; 0 on invalid arguments. */
 size_t llama_generate_workspace_bytes(const llama_args *a, int32_t batch, int32_t max_prompt_len);
 
-#define LLAMA_GEN_NO_GRAPH 1
+#define LLAMA_GEN_GRAPH 2
 
 /* Autoregressive generation [P2 6 generate; P3 4]: each sequence's prompt,
  * then one model choice per position.
@@ -243,9 +243,12 @@ size_t llama_generate_workspace_bytes(const llama_args *a, int32_t batch, int32_
  *   out_len     [batch] int32 (device, out): the number of tokens before the
  *               first eos_id in tokens[b] (the pages cut the output there),
  *               else the sequence's length
- *   flags       LLAMA_GEN_NO_GRAPH: launch each step's kernels one by one
- *               instead of replaying a captured HIP graph (graphs also need
- *               a stream other than the null stream)
+ *   flags       LLAMA_GEN_GRAPH: capture one step (decode, choice, state
+ *               update) as a HIP graph and replay it, instead of launching
+ *               its kernels one by one (needs a stream other than the null
+ *               stream; on this stack the two measure alike at 8B shapes and
+ *               the graph is slightly slower on small models).  A stream that
+ *               is itself being captured is not supported.
  *   steps_run   HOST (nullable): decode steps run
  * The prompts are right-padded to the longest one and prefilled together
  * (at most 16384 tokens per call), each sequence's first token taken from its

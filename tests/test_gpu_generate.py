@@ -137,7 +137,7 @@ def test_generate_greedy_ragged_prompts_graph_and_eager():
     toks, out_len, steps = _run_generate(dm, args, prompt, lens, 10, -1)
     assert steps == 9
     _check_against_oracle(cfg, prompt, lens, toks, out_len, 10, -1, args.max_seq_len, GAP_EXEMPT, dm=dm, args=args)
-    toks2, out_len2, _ = _run_generate(dm, args, prompt, lens, 10, -1, flags=M.LLAMA_GEN_NO_GRAPH)
+    toks2, out_len2, _ = _run_generate(dm, args, prompt, lens, 10, -1, flags=M.LLAMA_GEN_GRAPH)
     assert np.array_equal(toks, toks2) and np.array_equal(out_len, out_len2)
     toks3, _, _ = _run_generate(dm, args, prompt, lens, 10, -1, side_stream=False)
     assert np.array_equal(toks, toks3)
@@ -198,7 +198,7 @@ def test_generate_sampled_fp32_model():
     _check_against_oracle(cfg, prompt, lens, toks, out_len, 16, -1, 40, GEN_SAMPLE_MARGIN, temp=0.6, top_p=0.9,
                           uniforms=U.astype(np.float64), min_decided=0.8)
     toks2, _, _ = _run_generate(dm, args, prompt, lens, 16, -1, temp=0.6, top_p=0.9, uniforms=U,
-                                flags=M.LLAMA_GEN_NO_GRAPH)
+                                flags=M.LLAMA_GEN_GRAPH)
     assert np.array_equal(toks, toks2)
 
 
