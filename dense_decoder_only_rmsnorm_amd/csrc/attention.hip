@@ -217,8 +217,10 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
   constexpr int TILE = KT * HD;     // elements per K or V tile
   constexpr int NT = HD / 16;       // S^T k-steps over head_dim
   constexpr int NO = HD / 32;       // O^T row blocks over head_dim
-  __shared__ __align__(16) u16 Ks[2][TILE];
-  __shared__ __align__(16) u16 Vs[2][TILE];
+  // one LDS object per stage: the compiler can then tell the stage being
+  // read from the one being filled and keeps the prefetch in flight
+  __shared__ __align__(16) u16 Ks0[TILE], Ks1[TILE];
+  __shared__ __align__(16) u16 Vs0[TILE], Vs1[TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;  // 8 waves
   const int n_rep = a.H / a.G;
@@ -280,16 +282,19 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
     lcol[i] = ((lane & 15) ^ (lrow[i] & 15)) * 8;
     lcolv[i] = ((lane & 15) ^ (((lrow[i] & 3) << 2) | ((lrow[i] >> 2) & 3))) * 8;
   }
-  auto issue = [&](int kt, int buf) {
+  auto issue = [&](int kt, auto buf_c) {
+    constexpr int BUF = decltype(buf_c)::value;
+    u16 *kd = BUF ? Ks1 : Ks0;
+    u16 *vd = BUF ? Vs1 : Vs0;
     const int k0 = kt * KT;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int key = min(k0 + lrow[i], kv_end - 1);  // rows past the end are masked
       const int p = __builtin_amdgcn_readfirstlane(wave + 8 * i);
       __builtin_amdgcn_global_load_lds((const void *)(Kg + (int64_t)key * kstride + lcol[i]),
-                                       (__attribute__((address_space(3))) void *)(Ks[buf] + p * 4 * HD), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void *)(kd + p * 4 * HD), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void *)(Vg + (int64_t)key * kstride + lcolv[i]),
-                                       (__attribute__((address_space(3))) void *)(Vs[buf] + p * 4 * HD), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void *)(vd + p * 4 * HD), 16, 0, 0);
     }
   };
 
@@ -307,30 +312,48 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
   const int jj = lane & 15, dg = (lane >> 4) & 1;
   const int vr0 = 4 * hf + (jj >> 2);
   const int vq = 2 * dg + ((jj & 3) >> 1), vhalf = (jj & 1) * 4;
+  // per-lane LDS element offsets, the same for both stages.  K: row lane%32,
+  // chunk (2t + hf) ^ (lane & 15) of head-dim step t (+32 rows for the second
+  // key block).  V^T: rows vr0 + 8*h2 (+16 per key step; the swizzle depends
+  // only on the row modulo 16) at output columns 32*ob + ...
+  int kofs[NT], vofs[NO][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) kofs[t] = (lane & 31) * HD + (((2 * t + hf) ^ (lane & 15)) * 8);
+#pragma unroll
+  for (int ob = 0; ob < NO; ++ob)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int r = vr0 + 8 * h2;
+      const int vsw = ((r & 3) << 2) | ((r >> 2) & 3);
+      vofs[ob][h2] = r * HD + (((4 * ob + vq) ^ vsw) * 8) + vhalf;
+    }
 
-  auto tile = [&](int kt, auto mask_c) {
+  auto tile = [&](int kt, auto mask_c, auto buf_c) {
     constexpr bool MASK = decltype(mask_c)::value;
+    constexpr int BUF = decltype(buf_c)::value;
     const int k0 = kt * KT;
-    const u16 *ks = Ks[kt & 1];
-    const u16 *vs = Vs[kt & 1];
+    // z is 0, opaque to the compiler: addresses are formed here from the
+    // shared offsets instead of being kept per stage across the loop
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    const u16 *ks = (BUF ? Ks1 : Ks0) + z;
+    const u16 *vs = (BUF ? Vs1 : Vs0) + z;
     // S^T = K Q^T: two 32-key blocks; K rows kb*32 + lane%32
     f32x16 sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
-    const u16 *krow = ks + (lane & 31) * HD;
-    const int isw = lane & 15;
     bf16x8 kf[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) kf[0][kb] = *reinterpret_cast<const bf16x8 *>(krow + kb * 32 * HD + ((hf ^ isw) * 8));
+    for (int kb = 0; kb < 2; ++kb) kf[0][kb] = *reinterpret_cast<const bf16x8 *>(ks + kofs[0] + kb * 32 * HD);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cb = t & 1;
       if (t + 1 < NT) {
-        const int co = ((2 * (t + 1) + hf) ^ isw) * 8;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) kf[cb ^ 1][kb] = *reinterpret_cast<const bf16x8 *>(krow + kb * 32 * HD + co);
+        for (int kb = 0; kb < 2; ++kb)
+          kf[cb ^ 1][kb] = *reinterpret_cast<const bf16x8 *>(ks + kofs[t + 1] + kb * 32 * HD);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -385,7 +408,6 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
       bf16x8 pf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sc[kb][8 * t + e];
-      const int rbase = 16 * ksp + vr0;
 #pragma unroll
       for (int ob = 0; ob < NO; ++ob) {
         typedef short v4s __attribute__((ext_vector_type(4)));
@@ -393,11 +415,9 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
         u32x2 wv[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          const int r = rbase + 8 * h2;
-          const int vsw = ((r & 3) << 2) | ((r >> 2) & 3);
-          const int off = (r * HD + (((4 * ob + vq) ^ vsw) * 8) + vhalf) * (int)sizeof(u16);
+          const u16 *src = vs + vofs[ob][h2] + 16 * ksp * HD;
           const v4s w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s *)((__attribute__((address_space(3))) const char *)vs + off));
+              (__attribute__((address_space(3))) v4s *)(const __attribute__((address_space(3))) u16 *)src);
           wv[h2] = __builtin_bit_cast(u32x2, w);
         }
         const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(wv[0].x, wv[0].y, wv[1].x, wv[1].y));
@@ -410,23 +430,46 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
   // masked, and tiles past the wave's last query are skipped.  Every wave
   // passes the same ntiles barriers.
   const int nfull = min(ntiles, (wmin + 1) / KT);
-  issue(kt_first, kt_first & 1);
-  for (int kt = kt_first; kt < ntiles; ++kt) {
-    __syncthreads();  // tile kt has landed; every wave is done with tile kt-1
-    if (kt + 1 < ntiles) issue(kt + 1, (kt + 1) & 1);
+  using Plain = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  auto step = [&](int kt, auto buf_c) {
+    constexpr int BUF = decltype(buf_c)::value;
+    // the only loads in flight are this wave's pieces of tile kt: wait for
+    // them, then the barrier makes the whole tile visible (and every wave is
+    // done with tile kt-1, whose stage the prefetch below overwrites).  A
+    // wave that skips tiles must still wait here for its pieces.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (kt + 1 < ntiles) issue(kt + 1, std::integral_constant<int, 1 - BUF>());
+    const int k0 = kt * KT;
     if (DOC) {
       // skip tiles wholly below the wave's lowest bound or past its last query
-      const int k0 = kt * KT;
-      if (k0 + KT - 1 < wlo_min || k0 > wmax) continue;
+      if (k0 + KT - 1 < wlo_min || k0 > wmax) return;
       if (k0 >= wlo_max && kt < nfull)
-        tile(kt, std::integral_constant<bool, false>());
+        tile(kt, Plain(), buf_c);
       else
-        tile(kt, std::integral_constant<bool, true>());
+        tile(kt, Masked(), buf_c);
     } else if (kt < nfull) {
-      tile(kt, std::integral_constant<bool, false>());
-    } else if (kt * KT <= wmax) {
-      tile(kt, std::integral_constant<bool, true>());
+      tile(kt, Plain(), buf_c);
+    } else if (k0 <= wmax) {
+      tile(kt, Masked(), buf_c);
     }
+  };
+  // tile kt lives in stage kt & 1; the loop runs two tiles per pass so that
+  // both stages are compile-time constants
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  int kt = kt_first;
+  if (kt & 1) {
+    issue(kt, S1());
+    step(kt, S1());
+    ++kt;
+  } else {
+    issue(kt, S0());
+  }
+  for (; kt < ntiles; kt += 2) {
+    step(kt, S0());
+    if (kt + 1 < ntiles) step(kt + 1, S1());
   }
 
   // lane holds O^T[d = 32*ob + 8*(r/4) + 4*hf + r%4][query lane%32]
