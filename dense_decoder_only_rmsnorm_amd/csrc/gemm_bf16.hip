@@ -45,8 +45,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.x * BM;
-  const int n0 = blockIdx.y * BN;
+  // Tile order.  Workgroups go to the eight XCDs round-robin by linear id.
+  // When both tile counts are multiples of 16, each run of 256 consecutive
+  // ids covers a 16 x 16 block of tiles (M-blocks first), and the 32 tiles
+  // one XCD receives from it form a 4 x 8 rectangle, so each XCD's L2 sees
+  // four A row-blocks and eight B row-blocks per k-chunk, and the chip as a
+  // whole works through the operands one 16 x 16 block at a time.
+  int bm = blockIdx.x, bn = blockIdx.y;
+  if ((gridDim.x & 15) == 0 && (gridDim.y & 15) == 0) {
+    const int L = blockIdx.x + blockIdx.y * gridDim.x;
+    const int sr = L >> 8, i = L & 255, x = i & 7, j = i >> 3;
+    const int smt = gridDim.x >> 4;
+    bm = 16 * (sr % smt) + 4 * (x & 3) + (j & 3);
+    bn = 16 * (sr / smt) + 8 * (x >> 2) + (j >> 2);
+  }
+  const int m0 = bm * BM;
+  const int n0 = bn * BN;
   const int K = a.K;
 
   // Loader: wave w fills tile rows 8j..8j+7 for j = w*AI + i (A) and w*BI + i
