@@ -114,7 +114,8 @@ def cpu_threads():
 
 
 def cpu_baseline_prefill(cfg, F):
-    """fp64 oracle on a bounded sample of the prefill workload."""
+    """fp64 oracle on a bounded sample of the prefill workload: the first 2048
+    tokens through 8 of the 32 layers, scaled to the whole prefill."""
     import numpy as np
 
     import inputs as I
@@ -242,8 +243,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        msg = ("bench.py measures one GPU only: this build runs the whole forward pass on a single MI355X "
-               "(multi-GPU sharding is described in DESIGN.md, not implemented); rerun with --gpus 1")
+        msg = ("bench.py measures one GPU only: the library runs the whole forward pass on a single MI355X "
+               "and implements no multi-GPU sharding; rerun with --gpus 1")
         log(msg)
         sys.exit(2)
 

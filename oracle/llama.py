@@ -17,7 +17,7 @@ Pages cited (by title and section):
   [P3] "大语言模型实现llama3-from-scratch：输出层与预测" (agent.csdn.net)
   [P4] joto.ai blog post on the Llama architecture (GQA, RoPE, RMSNorm)
 
-Readings where the pages are silent or disagree (each is repeated in the design doc):
+Readings where the pages are silent or disagree:
   * RoPE pairs are adjacent elements (2i, 2i+1) of a head (P1 6.6; P2 3.2),
     not the rotate-half convention.
   * theta_i = rope_theta ** (-2i / head_dim), i < head_dim/2 (P2 3.2, whose
