@@ -158,14 +158,6 @@ struct Carver {
   }
 };
 
-int ksplit_for(int nblk, int K) {
-  // enough blocks to cover the 256 compute units about 1.5 times, K slices
-  // remaining multiples of 128 (four waves x 32)
-  int ks = 1;
-  while (nblk * ks < 384 && ks < 16 && K % (ks * 2 * 128) == 0) ks *= 2;
-  return ks;
-}
-
 // ------------------------------- prefill layout ------------------------------
 struct PrefillWs {
   float *h;        // residual stream [T][D] fp32 (llama_prefill only)
@@ -229,7 +221,7 @@ HeadWs carve_head(Carver &c, const Dims &d, int M) {
   w.last = c.take<float>((size_t)M * d.D);
   if (d.dt == LLAMA_BF16) {
     w.hf = c.take<u16>((size_t)2 * M * d.D);
-    w.nblk = skinny_nblk(d.V, SK_LOGITS);
+    w.nblk = skinny_nblk(d.V, d.D, SK_LOGITS);
   } else {
     w.hf32 = c.take<float>((size_t)M * d.D);
     w.logits = c.take<float>((size_t)M * d.V);
@@ -260,9 +252,9 @@ struct DecodeWs {
 
 DecodeWs carve_decode(Carver &c, const Dims &d, int B, int cap) {
   DecodeWs w{};
-  w.ks1 = ksplit_for(skinny_nblk(d.Nqkv(), SK_PARTIAL), d.D);
-  w.ks2 = ksplit_for(skinny_nblk(d.D, SK_PARTIAL), d.Hq());
-  w.ks3 = ksplit_for(skinny_nblk(d.D, SK_PARTIAL), d.F);
+  w.ks1 = skinny_ksplit(d.Nqkv(), d.D);
+  w.ks2 = skinny_ksplit(d.D, d.Hq());
+  w.ks3 = skinny_ksplit(d.D, d.F);
   w.nchunk = (cap + kDecodeChunk - 1) / kDecodeChunk;
   const size_t Bz = (size_t)B;
   w.h = c.take<float>(Bz * d.D);

@@ -151,7 +151,11 @@ hipError_t launch_gemm_bf16(int epi, const GemmArgs &a, hipStream_t s);
 hipError_t launch_gemm_f32(int epi, const float *A, const float *B, float *C, int64_t ldc, const float *R,
                            int64_t ldr, int M, int N, int K, hipStream_t s);
 
-int skinny_nblk(int N, int epi);
+// Weight rows per block (64 or 128), row blocks (grid.x) and, for SK_PARTIAL,
+// K slices (grid.y): workspace sizing and the launch use the same rule.
+int skinny_rows(int N, int K, int epi);
+int skinny_nblk(int N, int K, int epi);
+int skinny_ksplit(int N, int K);
 hipError_t launch_skinny(int epi, const SkinnyArgs &a, hipStream_t s);
 
 hipError_t launch_attn_prefill(int dtype, const AttnArgs &a, hipStream_t s);

@@ -7,17 +7,20 @@
 // carrying ~16 significant bits; both planes are multiplied against the same
 // weight fragment (two MFMAs), so the weight bytes do not change.
 //
-// A block of 512 threads owns 64 B-rows and one K slice (grid.y).  The K
-// slice streams through two LDS stages of 64 k: weights and both activation
-// planes arrive with global_load_lds_dwordx4 in fully coalesced 1 KB pieces
-// (8 rows x 128 bytes), stored with the 16-byte chunk swizzle
-// c ^ ((row >> 1) & 7) so the MFMA fragment reads of 16 consecutive rows are
-// bank-conflict free.  The activations are shared by all waves through LDS.
-// Waves w and w+4 own the same 16 B-rows and split each 64-k stage into its
-// two 32-k halves; their partial sums meet in LDS at the end.  Small stages
-// and eight waves per block leave room for three blocks per compute unit:
-// the weight stream is latency-bound, and resident waves, more than a deeper
-// pipeline per block, are what keep enough loads in flight.
+// A block of 8*NR threads owns NR = 64 or 128 B-rows and one K slice
+// (grid.y).  The K slice streams through two LDS stages of 64 k: weights and
+// both activation planes arrive with global_load_lds_dwordx4 in fully
+// coalesced 1 KB pieces (8 rows x 128 bytes), stored with the 16-byte chunk
+// swizzle c ^ ((row >> 1) & 7) so the MFMA fragment reads of 16 consecutive
+// rows are bank-conflict free.  The activations are shared by all waves
+// through LDS.  Waves w and w + NR/16 own the same 16 B-rows and split each
+// 64-k stage into its two 32-k halves; their partial sums meet in LDS at the
+// end.  Small stages leave room for three 64-row or two 128-row blocks per
+// compute unit: the weight stream is latency-bound, and resident waves, more
+// than a deeper pipeline per block, keep enough loads in flight.  The
+// activation pieces are two thirds of a 64-row stage; 128-row blocks halve
+// that share, which pays wherever it still leaves enough blocks (the LM head,
+// and split-K products whose K slices stay at 512 or more).
 // MFMA 16x16x32 (v_mfma_f32_16x16x32_bf16): lane l supplies row/column
 // (l % 16) and eight consecutive k at 8*(l / 16); output register r of lane
 // l holds row 4*(l/16) + r, column l % 16.
@@ -40,31 +43,35 @@ constexpr int SK_KCH = 64;     // k per LDS stage
 constexpr int SK_STAGES = 2;
 constexpr int SK_ROWB = SK_KCH * 2;  // bytes per tile row (128)
 
-template <int MB, int EPI>
-__global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a) {
-  // stage layout (bf16): A hi [64][64], A lo [64][64], B [64][64]
-  constexpr int ST_ELEMS = 3 * 64 * SK_KCH;
+template <int NR, int MB, int EPI>
+__global__ __launch_bounds__(NR * 8) void skinny_kernel(SkinnyArgs a) {
+  constexpr int NT = NR * 8, NW = NT / 64;  // threads, waves
+  // stage layout (bf16): A hi [64][64], A lo [64][64], B [NR][64]
+  constexpr int ST_ELEMS = (128 + NR) * SK_KCH;
   extern __shared__ __align__(16) u16 sm[];  // [SK_STAGES][ST_ELEMS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wcol = wave & 3, khalf = wave >> 2;
+  const int wcol = wave % (NW / 2), khalf = wave / (NW / 2);
   const int nblk0 = blockIdx.x;
   const int ks = blockIdx.y;
   const int Kc = a.K / a.ksplit;
   const int kbeg = ks * Kc;
   const int nchunk = Kc / SK_KCH;
 
-  // Loader: 24 pieces of 1 KB per stage (A hi 8, A lo 8, B 8); wave w issues
-  // pieces w, w+8, w+16.  Piece p covers tile rows 8*(p%8) .. +7 of its matrix;
-  // lane L -> row 8*(p%8) + L/8, physical chunk L%8 holding logical chunk
-  // (L%8) ^ ((row >> 1) & 7).  Rows past M or past the weight read a clamped
-  // valid row: they only feed outputs that are never stored.
+  // Loader: 16 + NR/8 pieces of 1 KB per stage (A hi 8, A lo 8, B NR/8),
+  // piece p at stage offset 512*p; wave w issues pieces w, w + NW, ...
+  // Piece p covers rows 8*(p%8) .. +7 of A hi (p < 8) or A lo (p < 16), else
+  // rows 8*(p-16) .. +7 of B; lane L -> row 8*(piece row) + L/8, physical
+  // chunk L%8 holding logical chunk (L%8) ^ ((row >> 1) & 7).  Rows past M or
+  // past the weight read a clamped valid row: they only feed outputs that are
+  // never stored.
+  constexpr int NP = (16 + NR / 8) / NW;  // pieces per wave: 3 (NR 64), 2 (NR 128)
   const int lr = lane >> 3, lq = lane & 7;
-  const u16 *src[3];
+  const u16 *src[NP];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int p = wave + 8 * i;        // 0..23
-    const int mat = p >> 3;            // 0: A hi, 1: A lo, 2: B
-    const int row = (p & 7) * 8 + lr;  // tile row 0..63
+  for (int i = 0; i < NP; ++i) {
+    const int p = wave + NW * i;
+    const int mat = p < 16 ? (p >> 3) : 2;  // 0: A hi, 1: A lo, 2: B
+    const int row = mat < 2 ? (p & 7) * 8 + lr : (p - 16) * 8 + lr;  // row of its matrix
     const int c = lq ^ ((row >> 1) & 7);
     const u16 *base;
     int64_t ld;
@@ -78,10 +85,10 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a) {
       if (EPI == SK_SWIGLU_HILO || EPI == SK_SWIGLU_BF16) {
         // tile rows: [gate 0-15 | up 0-15 | gate 16-31 | up 16-31] of this block's 32 output columns
         const int F = a.N / 2;
-        wr = min(nblk0 * 32 + (row >> 5) * 16 + (row & 15), F - 1);
+        wr = min(nblk0 * (NR / 2) + (row >> 5) * 16 + (row & 15), F - 1);
         base = ((row >> 4) & 1) ? a.B1 : a.B0;
       } else {
-        const int n = min(nblk0 * 64 + row, a.N - 1);
+        const int n = min(nblk0 * NR + row, a.N - 1);
         if (a.nq > 0) {
           base = n < a.nq ? a.B0 : (n < a.nq + a.nk ? a.B1 : a.B2);
           wr = n < a.nq ? n : (n < a.nq + a.nk ? n - a.nq : n - a.nq - a.nk);
@@ -98,9 +105,9 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a) {
   auto issue = [&](int stage, int chunk) {
     u16 *st = sm + stage * ST_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int p = __builtin_amdgcn_readfirstlane(wave + 8 * i);
-      u16 *dst = st + (p >> 3) * 64 * SK_KCH + (p & 7) * 8 * SK_KCH;
+    for (int i = 0; i < NP; ++i) {
+      const int p = __builtin_amdgcn_readfirstlane(wave + NW * i);
+      u16 *dst = st + p * 8 * SK_KCH;
       __builtin_amdgcn_global_load_lds((const void *)(src[i] + chunk * SK_KCH),
                                        (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
     }
@@ -138,40 +145,40 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a) {
   }
   __syncthreads();  // stages are reused for the epilogue
 
-  // wave pair (w, w+4) holds column block w%4: acc[mb][r] = partial
-  // C[mb*16 + 4*(lane/16) + r][16*(w%4) + lane%16] over its k halves
-  float *red = reinterpret_cast<float *>(sm);  // [MB*16 rows][64 cols]
+  // wave pair (w, w + NW/2) holds column block wcol: acc[mb][r] = partial
+  // C[mb*16 + 4*(lane/16) + r][16*wcol + lane%16] over its k halves
+  float *red = reinterpret_cast<float *>(sm);  // [MB*16 rows][NR cols]
   if (khalf == 0) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[(mb * 16 + 4 * (lane >> 4) + r) * 64 + wcol * 16 + frow] = acc[mb][r];
+      for (int r = 0; r < 4; ++r) red[(mb * 16 + 4 * (lane >> 4) + r) * NR + wcol * 16 + frow] = acc[mb][r];
   }
   __syncthreads();
   if (khalf == 1) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[(mb * 16 + 4 * (lane >> 4) + r) * 64 + wcol * 16 + frow] += acc[mb][r];
+      for (int r = 0; r < 4; ++r) red[(mb * 16 + 4 * (lane >> 4) + r) * NR + wcol * 16 + frow] += acc[mb][r];
   }
   __syncthreads();
   constexpr int ROWS = MB * 16;
 
   if (EPI == SK_PARTIAL) {
     float *C = static_cast<float *>(a.C) + (int64_t)ks * a.c_plane;
-    for (int e = tid; e < ROWS * 64; e += 512) {
-      const int row = e >> 6, col = nblk0 * 64 + (e & 63);
+    for (int e = tid; e < ROWS * NR; e += NT) {
+      const int row = e / NR, col = nblk0 * NR + e % NR;
       if (row < a.M && col < a.N) C[(int64_t)row * a.N + col] = red[e];
     }
   } else if (EPI == SK_SWIGLU_HILO || EPI == SK_SWIGLU_BF16) {
     const int F = a.N / 2;
     u16 *C = static_cast<u16 *>(a.C);
-    for (int e = tid; e < ROWS * 32; e += 512) {
-      const int row = e >> 5, uc = e & 31;
+    for (int e = tid; e < ROWS * (NR / 2); e += NT) {
+      const int row = e / (NR / 2), uc = e % (NR / 2);
       const int gc = (uc >> 4) * 32 + (uc & 15);  // gate column in the tile; up is 16 further
-      const int col = nblk0 * 32 + uc;
+      const int col = nblk0 * (NR / 2) + uc;
       if (row < a.M && col < F) {
-        const float g = red[row * 64 + gc], up = red[row * 64 + gc + 16];
+        const float g = red[row * NR + gc], up = red[row * NR + gc + 16];
         const float u = silu(g) * up;
         const int64_t o = (int64_t)row * F + col;
         if (EPI == SK_SWIGLU_HILO) {
@@ -186,8 +193,8 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a) {
     }
   } else {  // SK_LOGITS
     if (a.logits) {
-      for (int e = tid; e < ROWS * 64; e += 512) {
-        const int row = e >> 6, col = nblk0 * 64 + (e & 63);
+      for (int e = tid; e < ROWS * NR; e += NT) {
+        const int row = e / NR, col = nblk0 * NR + e % NR;
         if (row < a.M && col < a.N) a.logits[(int64_t)row * a.N + col] = red[e];
       }
     }
@@ -195,10 +202,10 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a) {
       const int row = tid;
       float bv = -INFINITY;
       int bi = 0x7fffffff;
-      for (int c = 0; c < 64; ++c) {
-        const int col = nblk0 * 64 + c;
+      for (int c = 0; c < NR; ++c) {
+        const int col = nblk0 * NR + c;
         if (col >= a.N) break;
-        const float v = red[row * 64 + c];
+        const float v = red[row * NR + c];
         if (v > bv) { bv = v; bi = col; }  // ascending columns: first maximum kept
       }
       if (row < a.M) {
@@ -209,43 +216,64 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a) {
   }
 }
 
-template <int MB, int EPI>
-hipError_t launch_one(const SkinnyArgs &a, dim3 grid, size_t lds, hipStream_t s) {
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny_kernel<MB, EPI>),
+template <int NR, int MB, int EPI>
+hipError_t launch_one(const SkinnyArgs &a, dim3 grid, hipStream_t s) {
+  // two stages; the epilogue's MB*16 x NR floats fit in the same space
+  constexpr size_t lds = (size_t)SK_STAGES * (128 + NR) * SK_KCH * sizeof(u16);
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny_kernel<NR, MB, EPI>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   (void)attr;
-  hipLaunchKernelGGL((skinny_kernel<MB, EPI>), grid, dim3(512), lds, s, a);
+  hipLaunchKernelGGL((skinny_kernel<NR, MB, EPI>), grid, dim3(NR * 8), lds, s, a);
   return hipGetLastError();
 }
 
-template <int MB>
+template <int NR, int MB>
 hipError_t launch_mb(int epi, const SkinnyArgs &a, hipStream_t s) {
-  const int nblk = (epi == SK_SWIGLU_HILO || epi == SK_SWIGLU_BF16) ? (a.N / 2 + 31) / 32 : (a.N + 63) / 64;
-  dim3 grid(nblk, a.ksplit);
-  const size_t lds = (size_t)SK_STAGES * 3 * 64 * SK_KCH * sizeof(u16);  // >= the epilogue's 64 x 64 floats
+  dim3 grid(skinny_nblk(a.N, a.K, epi), a.ksplit);
   switch (epi) {
-    case SK_PARTIAL: return launch_one<MB, SK_PARTIAL>(a, grid, lds, s);
-    case SK_SWIGLU_HILO: return launch_one<MB, SK_SWIGLU_HILO>(a, grid, lds, s);
-    case SK_SWIGLU_BF16: return launch_one<MB, SK_SWIGLU_BF16>(a, grid, lds, s);
-    case SK_LOGITS: return launch_one<MB, SK_LOGITS>(a, grid, lds, s);
+    case SK_PARTIAL: return launch_one<NR, MB, SK_PARTIAL>(a, grid, s);
+    case SK_SWIGLU_HILO: return launch_one<NR, MB, SK_SWIGLU_HILO>(a, grid, s);
+    case SK_SWIGLU_BF16: return launch_one<NR, MB, SK_SWIGLU_BF16>(a, grid, s);
+    case SK_LOGITS: return launch_one<NR, MB, SK_LOGITS>(a, grid, s);
   }
   return hipErrorInvalidValue;
+}
+
+template <int NR>
+hipError_t launch_nr(int epi, const SkinnyArgs &a, hipStream_t s) {
+  switch ((a.M + 15) / 16) {
+    case 1: return launch_mb<NR, 1>(epi, a, s);
+    case 2: return launch_mb<NR, 2>(epi, a, s);
+    case 3: return launch_mb<NR, 3>(epi, a, s);
+    case 4: return launch_mb<NR, 4>(epi, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// K slices for nblk row blocks: enough blocks to cover the 256 compute units
+// about 1.5 times, slices remaining multiples of 128
+int ksplit_rule(int nblk, int K) {
+  int ks = 1;
+  while (nblk * ks < 384 && ks < 16 && K % (ks * 2 * 128) == 0) ks *= 2;
+  return ks;
 }
 }  // namespace
 
-int skinny_nblk(int N, int epi) {
-  return (epi == SK_SWIGLU_HILO || epi == SK_SWIGLU_BF16) ? (N / 2 + 31) / 32 : (N + 63) / 64;
+int skinny_rows(int N, int K, int epi) {
+  if (epi == SK_SWIGLU_HILO || epi == SK_SWIGLU_BF16) return 64;  // 128 would leave CUs without a block
+  if (epi == SK_LOGITS) return 128;
+  return K / ksplit_rule((N + 127) / 128, K) >= 512 ? 128 : 64;
 }
 
+int skinny_nblk(int N, int K, int epi) {
+  const int nr = skinny_rows(N, K, epi);
+  return (epi == SK_SWIGLU_HILO || epi == SK_SWIGLU_BF16) ? (N / 2 + nr / 2 - 1) / (nr / 2) : (N + nr - 1) / nr;
+}
+
+int skinny_ksplit(int N, int K) { return ksplit_rule(skinny_nblk(N, K, SK_PARTIAL), K); }
+
 hipError_t launch_skinny(int epi, const SkinnyArgs &a, hipStream_t s) {
-  const int mb = (a.M + 15) / 16;
-  switch (mb) {
-    case 1: return launch_mb<1>(epi, a, s);
-    case 2: return launch_mb<2>(epi, a, s);
-    case 3: return launch_mb<3>(epi, a, s);
-    case 4: return launch_mb<4>(epi, a, s);
-  }
-  return hipErrorInvalidValue;
+  return skinny_rows(a.N, a.K, epi) == 128 ? launch_nr<128>(epi, a, s) : launch_nr<64>(epi, a, s);
 }
 
 }  // namespace llk
