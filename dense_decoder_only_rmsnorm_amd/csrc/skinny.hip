@@ -107,6 +107,9 @@ __global__ __launch_bounds__(NR * 8) void skinny_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int p = __builtin_amdgcn_readfirstlane(wave + NW * i);
+      // activation rows from MB*16 on are never read by the MFMAs (few rows:
+      // the prefill LM head, small decode batches): their pieces are skipped
+      if (p < 16 && (p & 7) * 8 >= MB * 16) continue;
       u16 *dst = st + p * 8 * SK_KCH;
       __builtin_amdgcn_global_load_lds((const void *)(src[i] + chunk * SK_KCH),
                                        (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
