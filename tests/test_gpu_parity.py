@@ -135,7 +135,10 @@ def test_prefill_c2_bf16():
 
 
 @pytest.mark.parametrize("dtype,D,H,G", [("bf16", 512, 8, 2), ("f32", 512, 8, 2), ("bf16", 1024, 8, 2),
-                                         ("bf16", 1024, 8, 1), ("bf16", 768, 8, 2)])
+                                         ("bf16", 1024, 8, 1), ("bf16", 768, 8, 2),
+                                         # hd 96: QKV has 1728 weight rows on 128-row blocks (ragged
+                                         # last block), wo 128-row blocks without a K split
+                                         ("bf16", 1152, 12, 3)])
 def test_decode_ragged_positions_match_oracle(dtype, D, H, G):
     # prefill S tokens into the cache, then one decode step with per-sequence positions
     cfg = small_cfg(dtype, D, H, G, 40, 3, L=2, V=3000, seed=21).with_(kind="prefill")
