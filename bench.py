@@ -30,18 +30,20 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
-# HBM bytes per launch of the roofline kernels, from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE runs (see the summary beside it); each entry records the
-# SHA-256 of the sources it was measured with
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# Per-kernel rocprofv3 counter figures (HBM bytes per launch from FETCH_SIZE
+# and WRITE_SIZE, MFMA busy %% from SQ_VALU_MFMA_BUSY_CYCLES over
+# GRBM_GUI_ACTIVE); each entry records the SHA-256 of the sources it was
+# measured with and is used only while they are unchanged
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of ``kernel`` from the committed counter summary,
-    or None when there is none or its sources changed since it was taken."""
+def measured(kernel, field):
+    """``field`` of ``kernel`` from the committed counter summary, or None
+    when there is none or the kernel's sources changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTERS_FILE) as f:
             entry = json.load(f)["kernels"][kernel]
+        value = entry[field]
     except (OSError, ValueError, KeyError):
         return None
     h = hashlib.sha256()
@@ -53,7 +55,11 @@ def measured_traffic(kernel):
             return None
     if h.hexdigest() != entry["sources_sha256"]:
         return None
-    return float(entry["bytes_per_launch"])
+    return None if value is None else float(value)
+
+
+def measured_traffic(kernel):
+    return measured(kernel, "bytes_per_launch")
 
 
 def log(*a):
@@ -70,6 +76,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the packed-document prefill and the generation loop measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the smaller configurations (tiny fp32 stack, small GQA stack, one 8B layer)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -101,6 +109,25 @@ def kernel_times(fn, steps, M, torch):
     return {k: {"launches": n // steps, "ms_per_step": ms / steps, "avg_ms": ms / n} for k, (n, ms) in rep.items()}
 
 
+def kernel_rooflines(kt, work):
+    """Rate and roofline fraction of each timed kernel from its algorithmic
+    work per launch (flop for "mfma", bytes for "hbm") and its event-timed
+    average launch duration, with the counter figures where measured."""
+    res = {}
+    for name, (bound, amount) in work.items():
+        if name not in kt:
+            continue
+        avg = kt[name]["avg_ms"]
+        if bound == "mfma":
+            ach, peak, unit = amount / (avg / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = amount / (avg / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s"
+        res[name] = {"bound": bound, "avg_ms": round(avg, 5), "achieved": round(ach, 2), "unit": unit,
+                     "frac": round(ach / peak, 4), "work_per_launch": amount,
+                     "traffic": measured_traffic(name), "mfma_busy_pct": measured(name, "mfma_busy_pct")}
+    return res
+
+
 def cpu_threads():
     try:
         import threadpoolctl
@@ -113,64 +140,94 @@ def cpu_threads():
     return os.cpu_count() or 1
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_info():
+    return {"cores": cpu_threads(), "cpu": cpu_model(), "os_cpu_count": os.cpu_count(), "blas_threads": cpu_threads()}
+
+
 def cpu_baseline_prefill(cfg, F):
-    """fp64 oracle on a bounded sample of the prefill workload: the first 2048
-    tokens through 8 of the 32 layers, scaled to the whole prefill."""
+    """fp64 oracle on a bounded sample of the prefill workload: layer 0 over
+    the full 8192 positions (every row; attention's quadratic cost included),
+    times the 32 layers, plus the embedding gather, final norm, LM head and
+    argmax of the last row, all timed."""
     import numpy as np
 
     import inputs as I
     from oracle import llama as OL
     from oracle import runner as OR
 
-    S_s, L_s = 2048, 8
     syn = I.SyntheticModel(cfg, F)
-    ids = I.prompt_ids(cfg)[:, :S_s]
-    emb = syn.rows("tok_embeddings", ids[0])
-    layers = [syn.layer(l) for l in range(L_s)]
+    ids = I.prompt_ids(cfg)[0]
     a = OR.args_of(cfg)
-    a["n_layers"] = L_s
-    h = emb
+    lw32 = syn.layer(0)
+    norm_w, w_out = syn.get("norm"), syn.get("output")
+    table = syn.get("tok_embeddings")
     t0 = time.perf_counter()
-    for l in range(L_s):
-        lw = {k: OL._f64(v) for k, v in layers[l].items()}
-        h = OL.layer_forward(h, lw, a, np.arange(S_s))
-    t = time.perf_counter() - t0
-    per_layer = t / L_s
-    tok_s = S_s / (per_layer * cfg.n_layers)
-    return {"value": tok_s, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"fp64 oracle prefill of the first {S_s} tokens through {L_s} of the {cfg.n_layers} layers "
-                      f"({t:.1f} s), scaled to all layers; weights generated beforehand, LM head excluded",
-            "seconds": t}
+    h = OL._f64(table[ids])
+    t_embed = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    lw = {k: OL._f64(v) for k, v in lw32.items()}
+    h = OL.layer_forward(h, lw, a, np.arange(cfg.seq_len))
+    t_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    hf = OL.rms_norm(h[-1:], norm_w, cfg.norm_eps)
+    OL.argmax_first(OL.lm_head(hf, w_out))
+    t_head = time.perf_counter() - t0
+    total = t_embed + cfg.n_layers * t_layer + t_head
+    return {"value": cfg.seq_len / total, "unit": "tokens/s", "kind": "oracle", **cpu_info(),
+            "sample": f"fp64 oracle: layer 0 over all {cfg.seq_len} positions ({t_layer:.1f} s) x {cfg.n_layers} "
+                      f"layers + embedding ({t_embed:.2f} s) + final norm, LM head and argmax of the last row "
+                      f"({t_head:.2f} s); weights generated beforehand, untimed",
+            "seconds": t_embed + t_layer + t_head}
 
 
-def cpu_baseline_decode(cfg, F):
+def cpu_baseline_decode(cfg, F, L_s=4):
+    """fp64 oracle on a bounded sample of the decode step: all 64 sequences
+    through L_s of the 32 layers (every layer has the same shapes and cache
+    length, so the step is 32/L_s times that), plus the final norm, LM head
+    and argmax of all 64 rows, timed."""
     import numpy as np
 
     import inputs as I
     from oracle import llama as OL
     from oracle import runner as OR
 
-    B_s, L_s = 32, 8
+    B = cfg.batch
     syn = I.SyntheticModel(cfg, F)
-    ids = I.prompt_ids(cfg).reshape(-1)[:B_s]
+    ids = I.prompt_ids(cfg).reshape(-1)
     emb = syn.rows("tok_embeddings", ids)
     layers = [syn.layer(l) for l in range(L_s)]
-    caches = [[{"k": I.kv_cache_block(cfg, l, "k", b, b + 1)[0], "v": I.kv_cache_block(cfg, l, "v", b, b + 1)[0]}
-               for l in range(L_s)] for b in range(B_s)]
+    blocks = [{w: I.kv_cache_block(cfg, l, w) for w in ("k", "v")} for l in range(L_s)]
+    norm_w, w_out = syn.get("norm"), syn.get("output")
     a = OR.args_of(cfg)
+    hs = [OL._f64(emb[b:b + 1]) for b in range(B)]
     t0 = time.perf_counter()
     for l in range(L_s):
         lw = {k: OL._f64(v) for k, v in layers[l].items()}
-        for b in range(B_s):
-            c = caches[b][l]
-            cache = {"k": c["k"], "v": c["v"]}
-            OL.layer_forward(emb[b:b + 1], lw, a, np.array([cfg.cache_len]), cache=cache)
-    t = time.perf_counter() - t0
-    tok_s = B_s / (t / L_s * cfg.n_layers)
-    return {"value": tok_s, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"fp64 oracle decode of {B_s} sequences (cache 4096) through {L_s} of the {cfg.n_layers} "
-                      f"layers ({t:.1f} s), scaled to all layers; LM head excluded",
-            "seconds": t}
+        for b in range(B):
+            cache = {"k": blocks[l]["k"][b], "v": blocks[l]["v"][b]}
+            hs[b] = OL.layer_forward(hs[b], lw, a, np.array([cfg.cache_len]), cache=cache)
+    t_layers = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    hf = OL.rms_norm(np.concatenate(hs), norm_w, cfg.norm_eps)
+    OL.argmax_first(OL.lm_head(hf, w_out))
+    t_head = time.perf_counter() - t0
+    total = t_layers * cfg.n_layers / L_s + t_head
+    return {"value": B / total, "unit": "tokens/s", "kind": "oracle", **cpu_info(),
+            "sample": f"fp64 oracle decode of all {B} sequences (cache {cfg.cache_len}) through {L_s} of the "
+                      f"{cfg.n_layers} layers ({t_layers:.1f} s, x {cfg.n_layers // L_s}) + final norm, LM head and "
+                      f"argmax of the {B} rows ({t_head:.2f} s); weights and caches generated beforehand, untimed",
+            "seconds": t_layers + t_head}
 
 
 def bench_long_layer(dm, cfg, M, I, R, torch):
@@ -239,6 +296,102 @@ def bench_generate(dm, cfg, M, I, R, np, torch, B=64, gen=32, cap=256, lmin=96, 
     return res
 
 
+PEAK_FP32_TFLOPS = 157.3  # MI355X fp32 (vector and matrix)
+
+
+def layer_flops(cfg, F, B, S):
+    """Algorithmic flop of one layer on B x S tokens: GEMMs 2*M*N*K, attention
+    4*hd*H per unmasked (query, key) pair."""
+    D, Hq, Hk, T = cfg.dim, cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim, B * S
+    gemm = 2.0 * T * D * (Hq + 2 * Hk) + 2.0 * T * Hq * D + 2.0 * T * D * 2 * F + 2.0 * T * F * D
+    return gemm + 4.0 * cfg.head_dim * cfg.n_heads * B * (S * (S + 1) / 2)
+
+
+def layer_weight_bytes(cfg, F):
+    D, Hq, Hk = cfg.dim, cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    esz = 2 if cfg.bf16 else 4
+    return esz * (D * (Hq + 2 * Hk) + Hq * D + 3 * D * F + 2 * D)
+
+
+def bench_configs(M, I, R, np, torch, steps):
+    """The smaller configurations: the tiny fp32 stack (1 x 256), the small
+    GQA stack (4 x 1024), and one 8B-shaped layer at 17 and 2048 positions.
+    Each is timed with HIP events over ``steps`` calls after warm-up; the
+    17-position layer is also timed cold (a 1 GiB buffer written before each
+    call evicts its 436 MB of weights from the 256 MB Infinity Cache)."""
+    res = {}
+    for key in ("c1", "c2"):
+        cfg = I.CONFIGS[key]
+        dm = R.DeviceModel(cfg)
+        B, S = cfg.batch, cfg.seq_len
+        args = dm.args
+        args.max_batch_size, args.max_seq_len = B, S
+        ids = torch.from_numpy(I.prompt_ids(cfg)).cuda()
+        logits = torch.empty((B, cfg.vocab_size), dtype=torch.float32, device="cuda")
+        nid = torch.empty(B, dtype=torch.int32, device="cuda")
+        ws = R.workspace(args, B, S)
+
+        def run():
+            M.llama_prefill(args, dm.struct, ids, B, S, kv=None, logits=logits, next_id=nid, ws=ws)
+
+        ms = time_steps(run, steps, 3, torch)
+        flop = cfg.n_layers * layer_flops(cfg, dm.F, B, S) + 2.0 * B * cfg.dim * cfg.vocab_size
+        tf = flop / (ms / 1e3) / 1e12
+        peak = PEAK_BF16_TFLOPS if cfg.bf16 else PEAK_FP32_TFLOPS
+        res[key] = {"workload": f"{cfg.n_layers}-layer stack dim {cfg.dim}, {cfg.n_heads}/{cfg.n_kv_heads} heads, "
+                                f"vocab {cfg.vocab_size}, {cfg.dtype}; prefill {B} x {S} + LM head",
+                    "ms": round(ms, 4), "tokens_per_s": round(B * S / (ms / 1e3), 1),
+                    "roofline": {"bound": "mfma" if cfg.bf16 else "fp32", "achieved": round(tf, 2),
+                                 "unit": "TFLOP/s", "peak": peak, "frac": round(tf / peak, 4), "flop": flop}}
+        log(f"{key}: {ms:.3f} ms, {B * S / (ms / 1e3):.0f} tokens/s, {tf:.1f} TFLOP/s")
+        del dm, ws, logits
+    for key in ("c3_s17", "c3_s2048"):
+        cfg = I.CONFIGS[key]
+        dm = R.DeviceModel(cfg, with_head=False)
+        S = cfg.seq_len
+        args = R.args_for(cfg, max_batch=1, max_seq=S)
+        x = torch.from_numpy(I.hidden_x(cfg)).cuda()
+        y = torch.empty_like(x)
+        ws = R.workspace(args, 1, S)
+
+        def run():
+            M.llama_layer_forward(args, dm.layers[0], x, y, 1, S, 0, kv=None, ws=ws)
+
+        ms = time_steps(run, steps, 3, torch)
+        entry = {"workload": f"one 8B-shaped layer, x ~ N(0,1) [1, {S}, 4096], bf16", "ms": round(ms, 4),
+                 "tokens_per_s": round(S / (ms / 1e3), 1)}
+        if key == "c3_s17":
+            wb = layer_weight_bytes(cfg, dm.F)
+            flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+            cold = []
+            for _ in range(steps):
+                flush.zero_()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                run()
+                e1.record()
+                torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1))
+            cms = float(np.median(cold))
+            del flush
+            gw, gc = wb / (ms / 1e3) / 1e9, wb / (cms / 1e3) / 1e9
+            entry.update(cold_ms=round(cms, 4), cold_tokens_per_s=round(S / (cms / 1e3), 1),
+                         roofline={"bound": "hbm", "bytes": wb, "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                                   "achieved_cold": round(gc, 1), "frac_cold": round(gc / PEAK_HBM_GBS, 4),
+                                   "achieved_warm": round(gw, 1), "frac_warm": round(gw / PEAK_HBM_GBS, 4)})
+            log(f"{key}: warm {ms:.4f} ms, cold {cms:.4f} ms ({gc:.0f} GB/s of weights)")
+        else:
+            flop = layer_flops(cfg, dm.F, 1, S)
+            tf = flop / (ms / 1e3) / 1e12
+            entry["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "unit": "TFLOP/s",
+                                 "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flop": flop}
+            log(f"{key}: {ms:.4f} ms, {tf:.1f} TFLOP/s")
+        res[key] = entry
+        del dm, x, y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -292,22 +445,30 @@ def main():
         log(f"prefill: {ms:.3f} ms/step, {B * S / (ms / 1e3):.0f} tokens/s")
         for k, v in sorted(kt.items(), key=lambda kv: -kv[1]["ms_per_step"]):
             log(f"  {k:22s} {v['launches']:5d} launches  {v['ms_per_step']:9.3f} ms/step  avg {v['avg_ms']:.4f} ms")
+        # per-kernel algorithmic work per launch (GEMM 2*M*N*K; attention 4*hd*H
+        # per unmasked (query, key) pair; the LM head is bound by its weight read)
+        D, Hq, Hk, T = c4.dim, c4.n_heads * c4.head_dim, c4.n_kv_heads * c4.head_dim, B * S
+        work = {"gemm_qkv_rope": ("mfma", 2.0 * T * D * (Hq + 2 * Hk)),
+                "gemm_wo_resid": ("mfma", 2.0 * T * Hq * D),
+                "gemm_w1w3_swiglu": ("mfma", 2.0 * T * D * 2 * F),
+                "gemm_w2_resid": ("mfma", 2.0 * T * F * D),
+                "attn_prefill": ("mfma", 4.0 * c4.head_dim * c4.n_heads * B * (S * (S + 1) / 2)),
+                "lm_head": ("hbm", 2.0 * c4.vocab_size * D)}
+        per_kernel = kernel_rooflines(kt, work)
+        total_flop = c4.n_layers * sum(work[k][1] for k in work if k != "lm_head") + 2.0 * B * D * c4.vocab_size
+        step_tflops = total_flop / (ms / 1e3) / 1e12
         # dominant kernel: the fused w1/w3 SwiGLU GEMM (47% of the layer FLOPs)
-        dk = kt["gemm_w1w3_swiglu"]
-        flop = 2.0 * B * S * c4.dim * (2 * F)
-        ach = flop / (dk["avg_ms"] / 1e3) / 1e12
-        total_flop = 0.0
-        D, Hq, Hk = c4.dim, c4.n_heads * c4.head_dim, c4.n_kv_heads * c4.head_dim
-        T = B * S
-        per_layer = 2.0 * T * D * (Hq + 2 * Hk) + 2.0 * T * Hq * D + 2.0 * T * D * 2 * F + 2.0 * T * F * D
-        attn = 4.0 * c4.head_dim * c4.n_heads * B * (S * (S + 1) / 2)
-        total_flop = c4.n_layers * (per_layer + attn) + 2.0 * B * D * c4.vocab_size
-        out["prefill"] = dict(ms=ms, tok_s=B * S / (ms / 1e3), step_tflops=total_flop / (ms / 1e3) / 1e12,
-                              roofline={"kernel": "gemm_w1w3_swiglu", "bound": "mfma", "achieved": round(ach, 2),
-                                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                        "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+        dk = per_kernel["gemm_w1w3_swiglu"]
+        out["prefill"] = dict(ms=ms, tok_s=B * S / (ms / 1e3), step_tflops=step_tflops, kernels=per_kernel,
+                              roofline={"kernel": "gemm_w1w3_swiglu", "bound": "mfma", "achieved": dk["achieved"],
+                                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dk["frac"],
                                         "traffic": measured_traffic("gemm_w1w3_swiglu"),
-                                        "flop_per_launch": flop, "avg_launch_ms": dk["avg_ms"]})
+                                        "mfma_busy_pct": measured("gemm_w1w3_swiglu", "mfma_busy_pct"),
+                                        "flop_per_launch": work["gemm_w1w3_swiglu"][1],
+                                        "avg_launch_ms": dk["avg_ms"],
+                                        "step": {"achieved": round(step_tflops, 2), "unit": "TFLOP/s",
+                                                 "frac": round(step_tflops / PEAK_BF16_TFLOPS, 4),
+                                                 "flop": total_flop}})
         if not args.no_extras:
             # the same prefill over packed documents (document-level mask)
             docs = I.document_ids(c4.seed, "bench_documents", B, S, 2048)
@@ -362,18 +523,24 @@ def main():
         log(f"decode: {ms:.3f} ms/step, {B / (ms / 1e3):.0f} tokens/s")
         for k, v in sorted(kt.items(), key=lambda kv: -kv[1]["ms_per_step"]):
             log(f"  {k:22s} {v['launches']:5d} launches  {v['ms_per_step']:9.3f} ms/step  avg {v['avg_ms']:.4f} ms")
-        dk = kt["attn_decode"]
-        kv_bytes = 2.0 * B * (P + 1) * c5.n_kv_heads * c5.head_dim * 2
-        ach = kv_bytes / (dk["avg_ms"] / 1e3) / 1e9
         D, Hq, Hk = c5.dim, c5.n_heads * c5.head_dim, c5.n_kv_heads * c5.head_dim
+        kv_bytes = 2.0 * B * (P + 1) * Hk * 2  # K and V of positions 0..P (the new one written)
+        work = {"skinny_qkv": ("hbm", 2.0 * D * (Hq + 2 * Hk)), "skinny_wo": ("hbm", 2.0 * Hq * D),
+                "skinny_w1w3_swiglu": ("hbm", 2.0 * 2 * F * D), "skinny_w2": ("hbm", 2.0 * F * D),
+                "attn_decode": ("hbm", kv_bytes), "lm_head": ("hbm", 2.0 * c5.vocab_size * D)}
+        per_kernel = kernel_rooflines(kt, work)
         w_layer = 2.0 * (D * (Hq + 2 * Hk) + Hq * D + 3 * D * F + 2 * D)
         step_bytes = c5.n_layers * (w_layer + kv_bytes) + 2.0 * c5.vocab_size * D + 2.0 * D
-        out["decode"] = dict(ms=ms, tok_s=B / (ms / 1e3), step_gbs=step_bytes / (ms / 1e3) / 1e9,
-                             step_frac=step_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
-                             roofline={"kernel": "attn_decode", "bound": "hbm", "achieved": round(ach, 1),
-                                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+        dk = per_kernel["attn_decode"]
+        step_gbs = step_bytes / (ms / 1e3) / 1e9
+        out["decode"] = dict(ms=ms, tok_s=B / (ms / 1e3), step_gbs=step_gbs, step_frac=step_gbs / PEAK_HBM_GBS,
+                             kernels=per_kernel,
+                             roofline={"kernel": "attn_decode", "bound": "hbm", "achieved": dk["achieved"],
+                                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dk["frac"],
                                        "traffic": measured_traffic("attn_decode"), "bytes_per_launch": kv_bytes,
-                                       "avg_launch_ms": dk["avg_ms"]})
+                                       "avg_launch_ms": dk["avg_ms"],
+                                       "step": {"achieved": round(step_gbs, 1), "unit": "GB/s",
+                                                "frac": round(step_gbs / PEAK_HBM_GBS, 4), "bytes": step_bytes}})
         del caches, kvs, ws
         torch.cuda.empty_cache()
 
@@ -386,6 +553,12 @@ def main():
                                                    lspan=17)
             out["generate_small"]["model"] = "dim 768, 4 layers, 8 heads / 2 KV heads, vocab 32000, bf16"
             del dm2
+
+    configs = None
+    if args.only is None and not args.no_configs:
+        del dm
+        torch.cuda.empty_cache()
+        configs = bench_configs(M, I, R, np, torch, max(args.steps, 10))
 
     cpu = {}
     if not args.no_cpu_baseline:
@@ -424,10 +597,14 @@ def main():
     if head == "prefill":
         res["prefill_step_tflops"] = round(out["prefill"]["step_tflops"], 1)
         res["prefill_step_mfma_frac"] = round(out["prefill"]["step_tflops"] / PEAK_BF16_TFLOPS, 4)
+        res["prefill_kernels"] = out["prefill"]["kernels"]
+    if "decode" in out:
+        res["decode_kernels"] = out["decode"]["kernels"]
+    if configs:
+        res["configs"] = configs
     if cpu:
         c = cpu.get(head)
         res["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items() if k != "seconds"}
-        res["cpu_baseline"]["cpu"] = platform.processor() or platform.machine()
         if head == "prefill" and "decode" in cpu:
             res["decode"]["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                              for k, v in cpu["decode"].items() if k != "seconds"}

@@ -106,7 +106,11 @@ int32_t ffn_hidden(const llama_args *a) {
   // [P2 3.5]: hidden = int(2 * (4 * dim) / 3); times the multiplier when set
   // (truncated); rounded up to a multiple of multiple_of.
   int64_t hidden = (int64_t)(2.0 * (4.0 * a->dim) / 3.0);
-  if (a->ffn_dim_multiplier > 0.f) hidden = (int64_t)((double)a->ffn_dim_multiplier * (double)hidden);
+  if (a->ffn_dim_multiplier > 0.f) {
+    const double scaled = (double)a->ffn_dim_multiplier * (double)hidden;
+    if (!(scaled < 2147483648.0)) return -1;  // also keeps the conversion below defined
+    hidden = (int64_t)scaled;
+  }
   const int64_t m = a->multiple_of;
   const int64_t f = m * ((hidden + m - 1) / m);
   return f > INT32_MAX ? -1 : (int32_t)f;
@@ -680,16 +684,19 @@ int llama_decode_step(const llama_args *a, const llama_model_w *w, const int32_t
   return llama_decode_step_docs(a, w, ids, pos, nullptr, batch, kv, logits, next_id, ws, ws_bytes, stream);
 }
 
-int llama_decode_step_docs(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *pos,
-                           const int32_t *doc_start, int32_t batch, const llama_kv *kv, float *logits,
-                           int32_t *next_id, void *ws, size_t ws_bytes, void *stream) {
-  Dims d;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of a decode step (everything but the workspace).
+int check_decode(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *pos, int32_t batch,
+                 const llama_kv *kv, int32_t *next_id, Dims &d) {
   if (int e = check_model(a, d)) return e;
   if (!w || !w->tok_embeddings || !w->norm || !w->output || (d.L > 0 && !w->layers))
     return fail(LLAMA_ERR_ARG, "model weight pointer is NULL");
   for (int l = 0; l < d.L; ++l)
     if (int e = check_layer_w(&w->layers[l])) return e;
-  if (!ids || !pos || !next_id || !ws || (d.L > 0 && !kv)) return fail(LLAMA_ERR_ARG, "ids, pos, kv, next_id or ws is NULL");
+  if (!ids || !pos || !next_id || (d.L > 0 && !kv)) return fail(LLAMA_ERR_ARG, "ids, pos, kv or next_id is NULL");
   for (int l = 0; l < d.L; ++l)
     if (!kv[l].k || !kv[l].v) return fail(LLAMA_ERR_ARG, "kv[%d] has a NULL pointer", l);
   if (batch < 1) return fail(LLAMA_ERR_ARG, "batch must be >= 1");
@@ -697,6 +704,19 @@ int llama_decode_step_docs(const llama_args *a, const llama_model_w *w, const in
   if (a->max_seq_len < 1) return fail(LLAMA_ERR_SHAPE, "max_seq_len < 1");
   if (d.dt == LLAMA_BF16 && batch > kSkinnyRows)
     return fail(LLAMA_ERR_UNSUPPORTED, "decode batch %d above %d rows", batch, kSkinnyRows);
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int llama_decode_step_docs(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *pos,
+                           const int32_t *doc_start, int32_t batch, const llama_kv *kv, float *logits,
+                           int32_t *next_id, void *ws, size_t ws_bytes, void *stream) {
+  Dims d;
+  if (int e = check_decode(a, w, ids, pos, batch, kv, next_id, d)) return e;
+  if (!ws) return fail(LLAMA_ERR_ARG, "ws is NULL");
   const int cap = a->max_seq_len;
   const size_t need = decode_bytes(d, batch, cap);
   if (ws_bytes < need) return fail(LLAMA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

@@ -57,7 +57,7 @@ struct GemmArgs {
 
 // Skinny bf16 GEMM for M <= 64 rows (decode, LM head): A given as hi/lo bf16
 // planes, weights streamed once.
-enum SkinnyEpi { SK_PARTIAL = 0, SK_SWIGLU_HILO = 1, SK_LOGITS = 2, SK_SWIGLU_BF16 = 3 };
+enum SkinnyEpi { SK_PARTIAL = 0, SK_SWIGLU_HILO = 1, SK_LOGITS = 2 };
 struct SkinnyArgs {
   const uint16_t *A; int64_t a_plane; int lda;  // [2][M][K] (hi, lo) bf16
   int use_lo;                                   // 0: hi only

@@ -13,26 +13,38 @@ namespace llk {
 // ---------------------------------------------------------------------------
 // Embedding lookup [P1 4; P2 4 tok_embeddings]: h[r, :] = E[ids[r], :] as fp32.
 // Ids outside [0, V) produce NaN rows instead of an out-of-bounds read.
-// One block per row, 8 elements per thread and step.
+// One block per row; each thread moves 16-byte pieces: 8 bf16 (or 4 fp32)
+// table elements per load, written as fp32 with 16-byte stores.  D must be a
+// multiple of 8 (bf16) or 4 (fp32); rows are 16-byte aligned.
 // ---------------------------------------------------------------------------
 template <typename TW>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ ids, const TW *__restrict__ E,
                                                     float *__restrict__ h, int D, int V) {
+  constexpr int EPL = 16 / sizeof(TW);  // table elements per 16-byte load
   const int r = blockIdx.x;
   const int id = ids[r];
   float *dst = h + (int64_t)r * D;
   const bool ok = id >= 0 && id < V;
   const TW *src = E + (int64_t)(ok ? id : 0) * D;
-  for (int i = threadIdx.x * 4; i < D; i += 256 * 4) {
-    float4 v;
-    if (ok) {
-      v = make_float4(Elem<TW>::load(src + i), Elem<TW>::load(src + i + 1), Elem<TW>::load(src + i + 2),
-                      Elem<TW>::load(src + i + 3));
+  const float qnan = __int_as_float(0x7fc00000);
+  for (int i = threadIdx.x * EPL; i < D; i += 256 * EPL) {
+    const uint4 raw = ok ? *reinterpret_cast<const uint4 *>(src + i) : make_uint4(0, 0, 0, 0);
+    if (EPL == 8) {
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      float4 lo, hi;
+      lo.x = __uint_as_float(w[0] << 16); lo.y = __uint_as_float(w[0] & 0xffff0000u);
+      lo.z = __uint_as_float(w[1] << 16); lo.w = __uint_as_float(w[1] & 0xffff0000u);
+      hi.x = __uint_as_float(w[2] << 16); hi.y = __uint_as_float(w[2] & 0xffff0000u);
+      hi.z = __uint_as_float(w[3] << 16); hi.w = __uint_as_float(w[3] & 0xffff0000u);
+      if (!ok) lo = hi = make_float4(qnan, qnan, qnan, qnan);
+      *reinterpret_cast<float4 *>(dst + i) = lo;
+      *reinterpret_cast<float4 *>(dst + i + 4) = hi;
     } else {
-      v = make_float4(__int_as_float(0x7fc00000), __int_as_float(0x7fc00000), __int_as_float(0x7fc00000),
-                      __int_as_float(0x7fc00000));
+      float4 v = make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z),
+                             __uint_as_float(raw.w));
+      if (!ok) v = make_float4(qnan, qnan, qnan, qnan);
+      *reinterpret_cast<float4 *>(dst + i) = v;
     }
-    *reinterpret_cast<float4 *>(dst + i) = v;
   }
 }
 

@@ -29,7 +29,6 @@
 //   SK_PARTIAL       fp32 split-K partial [ks][M][N] (summed by the consumer)
 //   SK_SWIGLU_HILO   B-rows interleave w1/w3 (16 each, twice per block);
 //                    u = silu(gate) * up written as hi/lo planes [P2 3.5]
-//   SK_SWIGLU_BF16   same, one bf16 plane
 //   SK_LOGITS        fp32 logits (optional) + per-block (max, argmax)
 //                    partials, smallest index on ties [P1 12; P3 4]
 #include "common.h"
@@ -82,7 +81,7 @@ __global__ __launch_bounds__(NR * 8) void skinny_kernel(SkinnyArgs a) {
       ld = a.lda;
     } else {
       int wr;
-      if (EPI == SK_SWIGLU_HILO || EPI == SK_SWIGLU_BF16) {
+      if (EPI == SK_SWIGLU_HILO) {
         // tile rows: [gate 0-15 | up 0-15 | gate 16-31 | up 16-31] of this block's 32 output columns
         const int F = a.N / 2;
         wr = min(nblk0 * (NR / 2) + (row >> 5) * 16 + (row & 15), F - 1);
@@ -173,7 +172,7 @@ __global__ __launch_bounds__(NR * 8) void skinny_kernel(SkinnyArgs a) {
       const int row = e / NR, col = nblk0 * NR + e % NR;
       if (row < a.M && col < a.N) C[(int64_t)row * a.N + col] = red[e];
     }
-  } else if (EPI == SK_SWIGLU_HILO || EPI == SK_SWIGLU_BF16) {
+  } else if (EPI == SK_SWIGLU_HILO) {
     const int F = a.N / 2;
     u16 *C = static_cast<u16 *>(a.C);
     for (int e = tid; e < ROWS * (NR / 2); e += NT) {
@@ -184,14 +183,10 @@ __global__ __launch_bounds__(NR * 8) void skinny_kernel(SkinnyArgs a) {
         const float g = red[row * NR + gc], up = red[row * NR + gc + 16];
         const float u = silu(g) * up;
         const int64_t o = (int64_t)row * F + col;
-        if (EPI == SK_SWIGLU_HILO) {
-          u16 hi, lo;
-          split_hilo(u, hi, lo);
-          C[o] = hi;
-          C[a.c_plane + o] = lo;
-        } else {
-          C[o] = f2bf(u);
-        }
+        u16 hi, lo;
+        split_hilo(u, hi, lo);
+        C[o] = hi;
+        C[a.c_plane + o] = lo;
       }
     }
   } else {  // SK_LOGITS
@@ -236,7 +231,6 @@ hipError_t launch_mb(int epi, const SkinnyArgs &a, hipStream_t s) {
   switch (epi) {
     case SK_PARTIAL: return launch_one<NR, MB, SK_PARTIAL>(a, grid, s);
     case SK_SWIGLU_HILO: return launch_one<NR, MB, SK_SWIGLU_HILO>(a, grid, s);
-    case SK_SWIGLU_BF16: return launch_one<NR, MB, SK_SWIGLU_BF16>(a, grid, s);
     case SK_LOGITS: return launch_one<NR, MB, SK_LOGITS>(a, grid, s);
   }
   return hipErrorInvalidValue;
@@ -263,14 +257,14 @@ int ksplit_rule(int nblk, int K) {
 }  // namespace
 
 int skinny_rows(int N, int K, int epi) {
-  if (epi == SK_SWIGLU_HILO || epi == SK_SWIGLU_BF16) return 64;  // 128 would leave CUs without a block
+  if (epi == SK_SWIGLU_HILO) return 64;  // 128 would leave CUs without a block
   if (epi == SK_LOGITS) return 128;
   return K / ksplit_rule((N + 127) / 128, K) >= 512 ? 128 : 64;
 }
 
 int skinny_nblk(int N, int K, int epi) {
   const int nr = skinny_rows(N, K, epi);
-  return (epi == SK_SWIGLU_HILO || epi == SK_SWIGLU_BF16) ? (N / 2 + nr / 2 - 1) / (nr / 2) : (N + nr - 1) / nr;
+  return epi == SK_SWIGLU_HILO ? (N / 2 + nr / 2 - 1) / (nr / 2) : (N + nr - 1) / nr;
 }
 
 int skinny_ksplit(int N, int K) { return ksplit_rule(skinny_nblk(N, K, SK_PARTIAL), K); }

@@ -272,14 +272,32 @@ class SyntheticModel:
         return normal_bits(c.seed, tensor_name(kind, layer), self.shape(kind), c.weight_std)
 
     def rows(self, kind: str, rows: np.ndarray) -> np.ndarray:
-        """Selected rows of a [rows, cols] weight (embedding lookups without the full table)."""
+        """Selected rows of a [rows, cols] weight (embedding lookups without the full table).
+
+        Each stream chunk the rows touch is drawn once (in parallel), however
+        many of the requested rows fall into it."""
         c = self.cfg
         name = tensor_name(kind)
         nrow, ncol = self.shape(kind)
+        n = nrow * ncol
+        rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+        need = set()
+        for r in np.unique(rows):
+            need.update(range(int(r) * ncol // CHUNK, ((int(r) + 1) * ncol - 1) // CHUNK + 1))
+
+        def job(ch):
+            lo, hi = ch * CHUNK, min(n, (ch + 1) * CHUNK)
+            return ch, normal(c.seed, name, (nrow, ncol), c.weight_std, c.bf16, start=lo, stop=hi)
+
+        with _cf.ThreadPoolExecutor(max(1, min(_THREADS, len(need)))) as ex:
+            chunks = dict(ex.map(job, sorted(need)))
         out = np.empty((len(rows), ncol), dtype=np.float32)
-        for i, r in enumerate(np.asarray(rows).reshape(-1)):
-            out[i] = normal(c.seed, name, (nrow, ncol), c.weight_std, c.bf16,
-                            start=int(r) * ncol, stop=(int(r) + 1) * ncol)
+        for i, r in enumerate(rows):
+            a, b = int(r) * ncol, (int(r) + 1) * ncol
+            for ch in range(a // CHUNK, (b - 1) // CHUNK + 1):
+                lo = max(a, ch * CHUNK)
+                hi = min(b, (ch + 1) * CHUNK)
+                out[i, lo - a:hi - a] = chunks[ch][lo - ch * CHUNK:hi - ch * CHUNK]
         return out
 
     def layer(self, l: int) -> dict:

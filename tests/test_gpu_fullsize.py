@@ -2,16 +2,20 @@
 benchmark times (32 layers, S = 8192 prefill; 64-sequence decode over a
 4096-long cache).
 
-The fp64 oracle cannot run the whole 32-layer stack at these sizes in
-seconds, so these tests compare outputs the oracle can compute one by one:
-
-* prefill: layer l is checked on sampled rows, with the oracle fed the GPU's
-  own hidden state entering layer l (from a prefill truncated to l layers);
-  the last layer's last row is carried on through the oracle's final RMSNorm
-  and LM head and compared with the GPU's logits and argmax;
-* decode: sampled sequences of the batch are run through all 32 layers by the
-  oracle over their own seeded caches.
+* prefill, end to end: the oracle's own 32-layer fp64 result (every row,
+  every layer, from the seeded token ids; stored by
+  ``tests/golden/make_prefill_8b_oracle.py``, which imports only the oracle
+  and the input generator) against the GPU's full ``llama_prefill``: last-row
+  logits over the whole vocabulary, the argmax, and sampled rows of the
+  hidden state after 1, 8, 16, 24 and 32 layers (drift across the stack);
+* prefill, layer by layer: layer l on sampled rows with the oracle fed the
+  GPU's own hidden state entering layer l, which isolates one layer's error
+  from the drift;
+* decode: every sequence of the 64-sequence batch run through all 32 layers
+  by the oracle over its own seeded cache.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -19,7 +23,7 @@ import torch
 import dense_decoder_only_rmsnorm_amd as M
 import inputs as I
 from dense_decoder_only_rmsnorm_amd import runtime as R
-from gpu_util import BF16_TOL, assert_argmax, assert_close, host, say
+from gpu_util import BF16_TOL, GAP_EXEMPT, assert_argmax, assert_close, host, say
 from oracle import llama as OL
 from oracle import runner as OR
 
@@ -27,10 +31,48 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
+GOLDEN_8B = os.path.join(os.path.dirname(__file__), "golden", "prefill_8b_s8192_oracle.npz")
+
+
 def _args_with_layers(args, n):
     a = type(args).from_buffer_copy(args)
     a.n_layers = n
     return a
+
+
+@pytest.mark.timeout(900)
+def test_c4_prefill_end_to_end_against_stored_oracle():
+    import hashlib
+    cfg = I.CONFIGS["c4"]
+    B, S, L = cfg.batch, cfg.seq_len, cfg.n_layers
+    z = np.load(GOLDEN_8B, allow_pickle=False)
+    ids = I.prompt_ids(cfg).astype(np.int32)
+    assert str(z["ids_sha256"]) == hashlib.sha256(np.ascontiguousarray(ids[0]).tobytes()).hexdigest(), \
+        "seeded token ids differ from the ones the stored oracle result was computed on"
+    rows, depths = [int(r) for r in z["rows"]], [int(d) for d in z["depths"]]
+    say(f"case c4 prefill end to end B={B} S={S} L={L}: generating and uploading 8B weights")
+    dm = R.DeviceModel(cfg)
+    idd = torch.from_numpy(ids).cuda()
+    ws = R.workspace(dm.args, B, S)
+    logits = torch.empty((B, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    nid = torch.empty(B, dtype=torch.int32, device="cuda")
+    hidden = torch.empty((B, S, cfg.dim), dtype=torch.float32, device="cuda")
+    for i, n in enumerate(depths):
+        say(f"  GPU prefill through {n} layers")
+        a = _args_with_layers(dm.args, n)
+        model = M.model_struct(dm.tok, dm.layers[:n], dm.norm, dm.output)
+        M.llama_prefill(a, model, idd, B, S, kv=None, hidden=hidden, logits=logits, next_id=nid, ws=ws)
+        torch.cuda.synchronize()
+        h = host(hidden)[0]
+        assert np.all(np.isfinite(h))
+        assert_close(h[rows], z["hidden_rows"][i].astype(np.float64), BF16_TOL,
+                     f"c4 hidden after {n} layers (rows {rows})")
+    assert depths[-1] == L
+    ref_logits = z["logits"][None]
+    got = host(logits)
+    assert_close(got, ref_logits, BF16_TOL, "c4 last-row logits (32 layers, oracle end to end)")
+    say(f"  oracle argmax {int(z['argmax'])}, top-2 gap {float(z['top2_gap']):.3e}; gpu {int(nid.cpu()[0])}")
+    assert_argmax(nid.cpu().numpy(), ref_logits, "c4 argmax (oracle end to end)")
 
 
 @pytest.mark.timeout(900)
@@ -73,21 +115,33 @@ def test_c4_prefill_8k_layerwise_sampled_rows():
             assert_argmax(np.array([am]), ref_logits, "c4 argmax")
 
 
-@pytest.mark.timeout(900)
-def test_c5_decode_32_layers_sampled_sequences():
-    cfg = I.CONFIGS["c5"]
-    B, P, cap, L = cfg.batch, cfg.cache_len, cfg.cache_cap, cfg.n_layers
-    say(f"case c5 decode B={B} cache {P} L={L}: generating and uploading weights and caches")
-    dm = R.DeviceModel(cfg)
+GOLDEN_8B_DECODE = os.path.join(os.path.dirname(__file__), "golden", "decode_8b_b64_oracle.npz")
+
+
+def _c5_caches(cfg):
+    B, P, cap = cfg.batch, cfg.cache_len, cfg.cache_cap
     caches = []
-    for l in range(L):
+    for l in range(cfg.n_layers):
         pair = []
         for which in ("k", "v"):
             t = torch.zeros((B, cap, cfg.n_kv_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
             t[:, :P] = R.bits_to_device(I.kv_cache_bits(cfg, l, which))
             pair.append(t)
         caches.append(tuple(pair))
+    return caches
+
+
+@pytest.mark.timeout(900)
+def test_c5_decode_32_layers_all_sequences():
+    import hashlib
+    cfg = I.CONFIGS["c5"]
+    B, P, cap, L = cfg.batch, cfg.cache_len, cfg.cache_cap, cfg.n_layers
+    z = np.load(GOLDEN_8B_DECODE, allow_pickle=False)
     ids = I.prompt_ids(cfg).reshape(-1).astype(np.int32)
+    assert str(z["ids_sha256"]) == hashlib.sha256(ids.tobytes()).hexdigest()
+    say(f"case c5 decode B={B} cache {P} L={L}: generating and uploading weights and caches")
+    dm = R.DeviceModel(cfg)
+    caches = _c5_caches(cfg)
     pos = torch.full((B,), P, dtype=torch.int32, device="cuda")
     logits = torch.empty((B, cfg.vocab_size), dtype=torch.float32, device="cuda")
     nid = torch.empty(B, dtype=torch.int32, device="cuda")
@@ -98,18 +152,40 @@ def test_c5_decode_32_layers_sampled_sequences():
     torch.cuda.synchronize()
     got_all = host(logits)
     assert np.all(np.isfinite(got_all)), "non-finite logits"
-    seqs = [0, 9, 18, 27, 36, 45, 54, 63]
-    say(f"  oracle decode of sequences {seqs} through {L} layers")
-    new_kv = []
-    ref = OR.decode(cfg, seqs, new_kv=new_kv)
-    got = got_all[seqs]
-    assert_close(got, ref["logits"], BF16_TOL, "c5 logits (sampled sequences)")
-    assert float(np.max(np.abs(got - ref["logits"]))) < 1e-3 * float(np.max(np.abs(ref["logits"])))
-    assert_argmax(nid.cpu().numpy()[seqs], ref["logits"], "c5 argmax (sampled sequences)")
-    for (bi, l, kn, vn) in new_kv:
-        if l in (0, L // 2, L - 1):
-            b = seqs[bi]
-            assert_close(host(caches[l][0][b, P]), kn, BF16_TOL, f"new k seq {b} layer {l}")
-            assert_close(host(caches[l][1][b, P]), vn, BF16_TOL, f"new v seq {b} layer {l}")
+
+    # all 64 sequences against the oracle's stored result: the logit tensor on
+    # its stored entries (the 32 largest and a fixed stride of ids per
+    # sequence), with the tolerance scaled by the tensor's max |logit|
+    scale = float(np.max(z["max_abs"]))
+    got_s = np.concatenate([np.take_along_axis(got_all, z["top_idx"], axis=1), got_all[:, z["stride_idx"]]], axis=1)
+    ref_s = np.concatenate([z["top_val"], z["stride_val"]], axis=1)
+    err = float(np.max(np.abs(got_s - ref_s)))
+    say(f"  c5 logits, 64 sequences x {ref_s.shape[1]} stored ids: max_err={err:.3e} max|ref|={scale:.3e}")
+    assert err <= BF16_TOL * scale
+    assert err <= 1e-3 * scale  # the hi/lo decode path is far inside the bar
+    gid = nid.cpu().numpy()
+    agree = int(np.sum(gid == z["argmax"]))
+    say(f"  c5 argmax: {agree}/{B} agree, min oracle top-2 gap {float(z['top2_gap'].min()):.3e}")
+    for b in range(B):
+        if gid[b] != z["argmax"][b]:
+            assert z["top2_gap"][b] < GAP_EXEMPT, f"seq {b}: gpu {gid[b]} vs oracle {z['argmax'][b]}"
+            # the chosen id must be among the oracle's near-maxima
+            row = dict(zip(z["top_idx"][b].tolist(), z["top_val"][b].tolist()))
+            assert gid[b] in row and z["top_val"][b][0] - row[gid[b]] < GAP_EXEMPT
+    # argmax computed from the GPU's own logits equals the fused argmax
+    assert np.array_equal(gid, np.argmax(got_all, axis=1))
+    for i, l in enumerate(int(x) for x in z["kv_layers"]):
+        gk = host(caches[l][0][:, P]).reshape(B, -1)
+        gv = host(caches[l][1][:, P]).reshape(B, -1)
+        assert_close(gk, z["new_k"][i].astype(np.float64), BF16_TOL, f"new k, 64 sequences, layer {l}")
+        assert_close(gv, z["new_v"][i].astype(np.float64), BF16_TOL, f"new v, 64 sequences, layer {l}")
     # untouched slots stay as seeded: the step writes slot P only
     assert torch.equal(caches[L - 1][0][:, P + 1:], torch.zeros_like(caches[L - 1][0][:, P + 1:]))
+
+    # a few sequences with the oracle run live, full logits
+    seqs = [0, 21, 42, 63]
+    say(f"  live oracle decode of sequences {seqs} through {L} layers")
+    ref = OR.decode(cfg, seqs)
+    got = got_all[seqs]
+    assert_close(got, ref["logits"], BF16_TOL, "c5 logits (live oracle, 4 sequences)")
+    assert_argmax(gid[seqs], ref["logits"], "c5 argmax (live oracle)")

@@ -184,6 +184,26 @@ def test_generate_edge_cases():
                           args=args)
 
 
+def test_generate_greedy_fp32_model_at_the_gap_bar():
+    # fp32 model: logits agree with the oracle to ~1e-6, so greedy generation is
+    # checked at the argmax bar itself (ids may differ only where the oracle's
+    # top-2 gap is below 1e-3) with no widening, and at least 90 % of the
+    # generated tokens must be decided by that bar
+    cfg = I.CONFIGS["c1"]
+    dm = R.DeviceModel(cfg)
+    args = dm.args
+    args.max_seq_len = 64
+    args.max_batch_size = 4
+    lens = [5, 12, 1, 30]
+    prompt = I.token_ids(cfg.seed, "generate_prompt_greedy_fp32", (4, 30), cfg.vocab_size)
+    say("c1 greedy generate (fp32), prompts [5, 12, 1, 30], 24 new tokens")
+    toks, out_len, steps = _run_generate(dm, args, prompt, lens, 24, -1)
+    assert steps == 23
+    _check_against_oracle(cfg, prompt, lens, toks, out_len, 24, -1, 64, GAP_EXEMPT, min_decided=0.9)
+    toks2, _, _ = _run_generate(dm, args, prompt, lens, 24, -1, flags=M.LLAMA_GEN_GRAPH)
+    assert np.array_equal(toks, toks2)
+
+
 def test_generate_sampled_fp32_model():
     cfg = I.CONFIGS["c1"]
     dm = R.DeviceModel(cfg)

@@ -27,9 +27,17 @@ LAYER_CASES = [
     ("bf16", 512, 4, 4, 70, 1),     # hd 128, MHA
     ("bf16", 1024, 8, 1, 200, 1),   # hd 128, MQA (n_rep 8)
     ("bf16", 1024, 8, 2, 300, 2),   # hd 128, n_rep 4, several 256-row tiles
+    ("bf16", 512, 4, 2, 300, 1),    # hd 128, n_rep 2
+    ("bf16", 2048, 16, 1, 100, 1),  # hd 128, n_rep 16 (16 positions per block)
+    ("bf16", 512, 8, 8, 90, 1),     # hd 64, MHA
+    ("bf16", 512, 8, 1, 150, 1),    # hd 64, n_rep 8
+    ("bf16", 1024, 16, 1, 140, 1),  # hd 64, n_rep 16 (8 positions per block)
+    ("bf16", 768, 8, 1, 100, 1),    # hd 96, n_rep 8
+    ("bf16", 1536, 16, 1, 70, 1),   # hd 96, n_rep 16
     ("f32", 256, 4, 2, 100, 2),
     ("f32", 384, 4, 1, 65, 1),
     ("f32", 512, 4, 4, 70, 1),
+    ("f32", 512, 8, 1, 50, 1),      # fp32, n_rep 8
 ]
 
 
@@ -138,7 +146,12 @@ def test_prefill_c2_bf16():
                                          ("bf16", 1024, 8, 1), ("bf16", 768, 8, 2),
                                          # hd 96: QKV has 1728 weight rows on 128-row blocks (ragged
                                          # last block), wo 128-row blocks without a K split
-                                         ("bf16", 1152, 12, 3)])
+                                         ("bf16", 1152, 12, 3),
+                                         # every decode-attention variant the argument checks admit:
+                                         # hd 64/96 at n_rep 8 (MFMA, 8 heads) and 16 (vector
+                                         # kernel), hd 128 at n_rep 16, fp32 at n_rep 8
+                                         ("bf16", 512, 8, 1), ("bf16", 768, 8, 1), ("bf16", 1024, 16, 1),
+                                         ("bf16", 1536, 16, 1), ("bf16", 2048, 16, 1), ("f32", 512, 8, 1)])
 def test_decode_ragged_positions_match_oracle(dtype, D, H, G):
     # prefill S tokens into the cache, then one decode step with per-sequence positions
     cfg = small_cfg(dtype, D, H, G, 40, 3, L=2, V=3000, seed=21).with_(kind="prefill")

@@ -65,3 +65,13 @@ def test_bits_match_values():
     assert np.array_equal(I.bf16_bits_to_f32(bits), I.normal(4, "t", (n,), 0.5, True))
     c5 = I.CONFIGS["c5"].with_(batch=2, cache_len=8, n_kv_heads=2, dim=128, n_heads=2)
     assert np.array_equal(I.bf16_bits_to_f32(I.kv_cache_bits(c5, 1, "v")), I.kv_cache_block(c5, 1, "v"))
+
+
+def test_model_rows_across_chunk_boundaries(monkeypatch):
+    # rows that straddle stream chunks are assembled from each chunk drawn once
+    monkeypatch.setattr(I, "CHUNK", 1000)
+    cfg = I.CONFIGS["c2"].with_(vocab_size=97, dim=96, n_heads=2, n_kv_heads=1)
+    m = I.SyntheticModel(cfg, 256)
+    full = m.get("tok_embeddings")
+    rows = np.array([0, 10, 11, 96, 10, 41, 42])
+    assert np.array_equal(m.rows("tok_embeddings", rows), full[rows])
