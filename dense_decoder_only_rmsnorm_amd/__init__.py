@@ -6,7 +6,8 @@ called through its C ABI (``include/llama_mi355x.h``).  PyTorch supplies
 device memory and streams.  The entry points keep the C names:
 ``llama_layer_forward``, ``llama_prefill``, ``llama_decode_step``,
 ``lm_head_argmax``, ``llama_sample_top_p``, ``llama_generate``,
-``llama_layer_forward_docs``, ``llama_prefill_docs``, ``llama_decode_step_docs``, plus
+``llama_layer_forward_docs``, ``llama_prefill_docs``, ``llama_decode_step_docs``,
+``llama_decode_step_noalloc``, plus
 ``llama_ffn_hidden_dim``, ``llama_workspace_bytes`` and
 ``llama_generate_workspace_bytes``.
 
@@ -29,7 +30,7 @@ ERROR_NAMES = {-1: "LLAMA_ERR_ARG", -2: "LLAMA_ERR_SHAPE", -3: "LLAMA_ERR_UNSUPP
 EXPORTED = ("llama_ffn_hidden_dim", "llama_workspace_bytes", "llama_layer_forward", "llama_prefill",
             "llama_decode_step", "lm_head_argmax", "llama_sample_top_p", "llama_generate_workspace_bytes",
             "llama_generate", "llama_layer_forward_docs", "llama_prefill_docs", "llama_decode_step_docs",
-            "llama_last_error",
+            "llama_decode_step_noalloc", "llama_decode_noalloc_max_bytes", "llama_last_error",
             "llama_timing_enable", "llama_timing_report")
 LLAMA_GEN_GRAPH = 2
 
@@ -88,6 +89,11 @@ def lib() -> ctypes.CDLL:
         L.llama_decode_step.argtypes = [A, ctypes.POINTER(llama_model_w), vp, vp, i32, ctypes.POINTER(llama_kv), vp,
                                         vp, vp, sz, vp]
         L.llama_decode_step.restype = ctypes.c_int
+        L.llama_decode_step_noalloc.argtypes = [A, ctypes.POINTER(llama_model_w), vp, vp, i32,
+                                                ctypes.POINTER(llama_kv), vp, vp, vp]
+        L.llama_decode_step_noalloc.restype = ctypes.c_int
+        L.llama_decode_noalloc_max_bytes.argtypes = []
+        L.llama_decode_noalloc_max_bytes.restype = sz
         L.lm_head_argmax.argtypes = [A, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         L.lm_head_argmax.restype = ctypes.c_int
         L.llama_layer_forward_docs.argtypes = [A, ctypes.POINTER(llama_layer_w), vp, vp, i32, i32, i32,
@@ -225,6 +231,19 @@ def llama_decode_step(args: llama_args, model, ids, pos, batch: int, kv, logits=
     rc = lib().llama_decode_step(ctypes.byref(args), ctypes.byref(m), _p(ids), _p(pos), batch, kv, _p(logits),
                                  _p(next_id), _p(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc)
+
+
+def llama_decode_step_noalloc(args: llama_args, model, ids, pos, batch: int, kv, logits=None, next_id=None,
+                              stream=None):
+    """llama_decode_step with the library's static scratch in place of a workspace."""
+    m = model[0]
+    rc = lib().llama_decode_step_noalloc(ctypes.byref(args), ctypes.byref(m), _p(ids), _p(pos), batch, kv,
+                                         _p(logits), _p(next_id), _stream(stream))
+    _check(rc)
+
+
+def llama_decode_noalloc_max_bytes() -> int:
+    return int(lib().llama_decode_noalloc_max_bytes())
 
 
 def llama_decode_step_docs(args: llama_args, model, ids, pos, doc_start, batch: int, kv, logits=None, next_id=None,

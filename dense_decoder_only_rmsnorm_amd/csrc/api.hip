@@ -707,6 +707,35 @@ int check_decode(const llama_args *a, const llama_model_w *w, const int32_t *ids
   return LLAMA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free decode step (llama_decode_step_noalloc): a
+// file-scope device array that every GPU the library runs on holds until the
+// process ends.  Host code never uses the array's name as an address: its
+// device address is taken once per device with hipGetSymbolAddress and kept.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)96 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on its first use).
+int scratch_on_current_device(void **out) {
+  int dev = -1;
+  const hipError_t eg = hipGetDevice(&dev);
+  if (eg != hipSuccess) return fail(LLAMA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(eg));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LLAMA_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(LLAMA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LLAMA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -889,6 +918,23 @@ int llama_decode_step_docs(const llama_args *a, const llama_model_w *w, const in
     if (int e = rmsnorm(d, 0, dw.h, 0, d.D, nullptr, 0, 0, w->norm, a->norm_eps, hw.hf32, 0, B, s)) return e;
   }
   return run_head(d, hw, w->output, B, logits, next_id, s);
+}
+
+size_t llama_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int llama_decode_step_noalloc(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *pos,
+                              int32_t batch, const llama_kv *kv, float *logits, int32_t *next_id, void *stream) {
+  Dims d;
+  if (int e = check_decode(a, w, ids, pos, batch, kv, next_id, d)) return e;
+  const size_t need = decode_bytes(d, batch, a->max_seq_len);
+  if (need > kScratchBytes)
+    return fail(LLAMA_ERR_WORKSPACE,
+                "decode step of %d sequences with max_seq_len %d needs %zu bytes of scratch; the library's static "
+                "scratch holds %zu",
+                batch, a->max_seq_len, need, kScratchBytes);
+  void *ws = nullptr;
+  if (int e = scratch_on_current_device(&ws)) return e;
+  return llama_decode_step_docs(a, w, ids, pos, nullptr, batch, kv, logits, next_id, ws, kScratchBytes, stream);
 }
 
 int lm_head_argmax(const llama_args *a, const float *h, const void *final_norm_w, const void *w_out, int32_t M,

@@ -189,6 +189,31 @@ int llama_decode_step_docs(const llama_args *a, const llama_model_w *w, const in
                            const int32_t *doc_start, int32_t batch, const llama_kv *kv, float *logits,
                            int32_t *next_id, void *ws, size_t ws_bytes, void *stream);
 
+/* llama_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It computes exactly what
+ * llama_decode_step computes (same kernels, bit-identical outputs) and
+ * allocates nothing: its scratch (the decode workspace) is a static device
+ * array of llama_decode_noalloc_max_bytes() = 96 MiB inside the library,
+ * one per GPU, held by every GPU the library runs on until the process ends.
+ * The scratch of the current device is used (its address is looked up once
+ * per device, on the first call there); `stream` must belong to that device.
+ * Every call on a GPU shares that GPU's scratch and leaves its contents
+ * behind: calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and must not be issued.  Nothing
+ * in the scratch needs to start at zero: every value the step reads is
+ * written earlier in the same step.
+ * Arguments: as llama_decode_step, minus ws/ws_bytes.
+ * Errors: as llama_decode_step; ERR_WORKSPACE when the step needs more
+ *   scratch than the static array holds (llama_workspace_bytes(a, batch, 1)
+ *   gives the need; e.g. 8B shapes at 64 sequences fit up to a max_seq_len
+ *   of about 11000); ERR_HIP when the scratch's address cannot be obtained. */
+int llama_decode_step_noalloc(const llama_args *a, const llama_model_w *w, const int32_t *ids, const int32_t *pos,
+                              int32_t batch, const llama_kv *kv, float *logits, int32_t *next_id, void *stream);
+
+/* Size in bytes of the static scratch of llama_decode_step_noalloc. */
+size_t llama_decode_noalloc_max_bytes(void);
+
 /* Output head on M hidden rows [P1 11-12; P3 1-4]:
  *   h [M][dim] fp32 (device); final_norm_w (nullable, dtype) applies the
  *   final RMSNorm first; w_out [vocab][dim] (dtype).

@@ -136,6 +136,14 @@ int main() {
   expect_error(llama_decode_step(&a, &model, ids, ids, 2, nullptr, nullptr, out, fake, huge, nullptr), LLAMA_ERR_ARG);
   expect_error(llama_decode_step_docs(&a, &model, ids, ids, ids, 0, kvs, nullptr, out, fake, huge, nullptr),
                LLAMA_ERR_ARG);
+  expect_error(llama_decode_step_noalloc(&a, &model, ids, nullptr, 2, kvs, nullptr, out, nullptr), LLAMA_ERR_ARG);
+  {
+    llama_args big = args8b(64, 131072);
+    llama_kv kv8[2] = {{fake, fake}, {fake, fake}};
+    expect_error(llama_decode_step_noalloc(&big, &model, ids, ids, 64, kv8, nullptr, out, nullptr),
+                 LLAMA_ERR_WORKSPACE);
+    EXPECT(llama_decode_noalloc_max_bytes() == ((size_t)96 << 20));
+  }
 
   // head, sampler, generation
   expect_error(lm_head_argmax(&a, xf, nullptr, fake, 0, nullptr, out, fake, huge, nullptr), LLAMA_ERR_ARG);

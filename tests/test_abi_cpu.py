@@ -118,6 +118,32 @@ def test_decode_and_head_argument_errors():
     assert rc == M.LLAMA_ERR_ARG  # ids NULL
 
 
+def test_noalloc_decode_argument_errors_and_scratch_limit():
+    # the allocation-free decode step validates like llama_decode_step and
+    # refuses a step whose workspace exceeds its static scratch, all before
+    # any HIP call
+    L = M.lib()
+    cap = M.llama_decode_noalloc_max_bytes()
+    assert cap == 96 << 20
+    layers = (M.llama_layer_w * 2)(_layer_fake(), _layer_fake())
+    model = M.llama_model_w(0x1000, ctypes.cast(layers, ctypes.POINTER(M.llama_layer_w)), 0x1000, 0x1000)
+    kvs = (M.llama_kv * 2)(M.llama_kv(0x1000, 0x1000), M.llama_kv(0x1000, 0x1000))
+    a = _args()
+    assert L.llama_decode_step_noalloc(ctypes.byref(a), ctypes.byref(model), FAKE, None, 2, kvs, None, FAKE,
+                                       None) == M.LLAMA_ERR_ARG
+    assert L.llama_decode_step_noalloc(ctypes.byref(a), ctypes.byref(model), FAKE, FAKE, 9, kvs, None, FAKE,
+                                       None) == M.LLAMA_ERR_SHAPE
+    big = _args(dim=4096, n_heads=32, n_kv_heads=8, vocab_size=128256, multiple_of=1024, ffn_dim_multiplier=1.3,
+                max_batch_size=64, max_seq_len=131072)
+    assert M.llama_workspace_bytes(big, 64, 1) > cap
+    rc = L.llama_decode_step_noalloc(ctypes.byref(big), ctypes.byref(model), FAKE, FAKE, 64, kvs, None, FAKE, None)
+    assert rc == M.LLAMA_ERR_WORKSPACE and b"scratch" in L.llama_last_error()
+    # the 64-sequence 8B-shaped step over a 4224-position cache fits
+    fits = _args(dim=4096, n_heads=32, n_kv_heads=8, vocab_size=128256, multiple_of=1024, ffn_dim_multiplier=1.3,
+                 max_batch_size=64, max_seq_len=4224)
+    assert M.llama_workspace_bytes(fits, 64, 1) <= cap
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="forces the no-device path; only meaningful without a GPU")
 def test_no_device_reports_hip_error():
     a = _args()
