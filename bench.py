@@ -109,7 +109,7 @@ def kernel_times(fn, steps, M, torch):
     return {k: {"launches": n // steps, "ms_per_step": ms / steps, "avg_ms": ms / n} for k, (n, ms) in rep.items()}
 
 
-def kernel_rooflines(kt, work):
+def kernel_rooflines(kt, work, counter_keys=None):
     """Rate and roofline fraction of each timed kernel from its algorithmic
     work per launch (flop for "mfma", bytes for "hbm") and its event-timed
     average launch duration, with the counter figures where measured."""
@@ -122,9 +122,10 @@ def kernel_rooflines(kt, work):
             ach, peak, unit = amount / (avg / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
         else:
             ach, peak, unit = amount / (avg / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s"
+        ck = (counter_keys or {}).get(name, name)
         res[name] = {"bound": bound, "avg_ms": round(avg, 5), "achieved": round(ach, 2), "unit": unit,
                      "frac": round(ach / peak, 4), "work_per_launch": amount,
-                     "traffic": measured_traffic(name), "mfma_busy_pct": measured(name, "mfma_busy_pct")}
+                     "traffic": measured_traffic(ck), "mfma_busy_pct": measured(ck, "mfma_busy_pct")}
     return res
 
 
@@ -454,7 +455,7 @@ def main():
                 "gemm_w2_resid": ("mfma", 2.0 * T * F * D),
                 "attn_prefill": ("mfma", 4.0 * c4.head_dim * c4.n_heads * B * (S * (S + 1) / 2)),
                 "lm_head": ("hbm", 2.0 * c4.vocab_size * D)}
-        per_kernel = kernel_rooflines(kt, work)
+        per_kernel = kernel_rooflines(kt, work, {"lm_head": "lm_head_prefill"})
         total_flop = c4.n_layers * sum(work[k][1] for k in work if k != "lm_head") + 2.0 * B * D * c4.vocab_size
         step_tflops = total_flop / (ms / 1e3) / 1e12
         # dominant kernel: the fused w1/w3 SwiGLU GEMM (47% of the layer FLOPs)
