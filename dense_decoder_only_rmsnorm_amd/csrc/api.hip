@@ -181,6 +181,14 @@ struct PrefillWs {
   int32_t *pidx;
   int nblk;
   int32_t *kv_lo;  // [B][S] lowest visible key per query (document mask)
+  // bf16 layers on at most kSkinnyRows tokens run on the skinny (weight
+  // streaming) kernels: hi/lo activations and split-K partials
+  u16 *xhl;        // [2][T][D]
+  float *qkv_part; // [ks1][T][Nqkv]
+  float *wo_part;  // [ks2][T][D]
+  u16 *uhl;        // [2][T][F]
+  float *w2_part;  // [ks3][T][D]
+  int ks1, ks2, ks3;
 };
 
 PrefillWs carve_prefill(Carver &c, const Dims &d, int B, int S) {
@@ -196,6 +204,16 @@ PrefillWs carve_prefill(Carver &c, const Dims &d, int B, int S) {
     w.v = c.take<u16>(T * d.Hk());
     w.o = c.take<u16>(T * d.Hq());
     w.u = c.take<u16>(T * d.F);
+    if (T <= (size_t)kSkinnyRows) {
+      w.ks1 = skinny_ksplit(d.Nqkv(), d.D);
+      w.ks2 = skinny_ksplit(d.D, d.Hq());
+      w.ks3 = skinny_ksplit(d.D, d.F);
+      w.xhl = c.take<u16>(2 * T * d.D);
+      w.qkv_part = c.take<float>((size_t)w.ks1 * T * d.Nqkv());
+      w.wo_part = c.take<float>((size_t)w.ks2 * T * d.D);
+      w.uhl = c.take<u16>(2 * T * d.F);
+      w.w2_part = c.take<float>((size_t)w.ks3 * T * d.D);
+    }
   } else {
     w.xn = c.take<float>(T * d.D);
     w.qkv = c.take<float>(T * d.Nqkv());
@@ -351,6 +369,99 @@ int run_head(const Dims &d, const HeadWs &hw, const void *w_out, int M, float *l
   return LLAMA_OK;
 }
 
+// One bf16 layer on T <= kSkinnyRows tokens: every projection streams its
+// weights once through the skinny kernels (the tiled GEMMs would leave most of
+// a 256-row tile empty and most compute units idle), with hi/lo activations
+// as in the decode step; RoPE and the cache write run in rope_qkv_kernel,
+// attention in the prefill attention kernel.  h = y may alias x_in.
+int run_layer_prefill_skinny(const llama_args *a, const Dims &d, const llama_layer_w *lw, const float *x_in,
+                             float *h, int B, int S, int start_pos, void *kc, void *vc, int cap,
+                             const PrefillWs &w, const int32_t *kv_lo, hipStream_t s) {
+  const int T = B * S;
+  const int64_t TD = (int64_t)T * d.D;
+  auto skinny = [&](const char *tag, int epi, const u16 *A, int64_t a_plane, int lda, int use_lo, const void *B0,
+                    const void *B1, const void *B2, int nq, int nk, int N, int K, int ks, void *C,
+                    int64_t c_plane) -> int {
+    SkinnyArgs sa{};
+    sa.A = A;
+    sa.a_plane = a_plane;
+    sa.lda = lda;
+    sa.use_lo = use_lo;
+    sa.B0 = static_cast<const u16 *>(B0);
+    sa.B1 = static_cast<const u16 *>(B1);
+    sa.B2 = static_cast<const u16 *>(B2);
+    sa.nq = nq;
+    sa.nk = nk;
+    sa.M = T;
+    sa.N = N;
+    sa.K = K;
+    sa.ksplit = ks;
+    sa.C = C;
+    sa.c_plane = c_plane;
+    LAUNCH(tag, launch_skinny(epi, sa, s));
+    return LLAMA_OK;
+  };
+  // a2: attention_norm -> hi/lo
+  if (int e = rmsnorm(d, 2, const_cast<float *>(x_in), 0, d.D, nullptr, 0, 0, lw->attention_norm, a->norm_eps, w.xhl,
+                      TD, T, s))
+    return e;
+  // a3: QKV partials
+  if (int e = skinny("skinny_qkv", SK_PARTIAL, w.xhl, TD, d.D, 1, lw->wq, lw->wk, lw->wv, d.Hq(), d.Hk(), d.Nqkv(),
+                     d.D, w.ks1, w.qkv_part, (int64_t)T * d.Nqkv()))
+    return e;
+  // a4-a5: sum of the partials, RoPE at start_pos + s, q as bf16, K/V to the cache
+  RopeQkvArgs ra{};
+  ra.part = w.qkv_part;
+  ra.nsplit = w.ks1;
+  ra.part_stride = (int64_t)T * d.Nqkv();
+  ra.rows = T;
+  ra.S = S;
+  ra.H = d.H;
+  ra.G = d.G;
+  ra.hd = d.hd;
+  ra.tab = w.tab;
+  ra.tab_mod = S;
+  ra.pos = nullptr;
+  ra.start_pos = start_pos;
+  ra.cap = cap;
+  ra.qbf = static_cast<u16 *>(w.q);
+  ra.kc = kc;
+  ra.vc = vc;
+  LAUNCH("rope_qkv", launch_rope_qkv(d.dt, ra, s));
+  // a6: causal GQA attention (bf16 output o)
+  AttnArgs at{};
+  at.q = w.q;
+  at.q_stride = d.Hq();
+  at.k = kc;
+  at.v = vc;
+  at.kcap = cap;
+  at.o = w.o;
+  at.B = B;
+  at.S = S;
+  at.H = d.H;
+  at.G = d.G;
+  at.hd = d.hd;
+  at.start_pos = start_pos;
+  at.scale = (float)(1.0 / sqrt((double)d.hd));
+  at.kv_lo = kv_lo;
+  LAUNCH("attn_prefill", launch_attn_prefill(d.dt, at, s));
+  // a8: wo partials, folded into h = x_in + o wo^T by the ffn_norm kernel
+  if (int e = skinny("skinny_wo", SK_PARTIAL, static_cast<const u16 *>(w.o), 0, d.Hq(), 0, lw->wo, nullptr, nullptr, 0,
+                     0, d.D, d.Hq(), w.ks2, w.wo_part, TD))
+    return e;
+  if (h != x_in) HIPCHK(hipMemcpyAsync(h, x_in, (size_t)TD * sizeof(float), hipMemcpyDeviceToDevice, s));
+  if (int e = rmsnorm(d, 2, h, 0, d.D, w.wo_part, w.ks2, TD, lw->ffn_norm, a->norm_eps, w.xhl, TD, T, s)) return e;
+  // a9: u = silu(xn2 w1^T) * (xn2 w3^T) as hi/lo
+  if (int e = skinny("skinny_w1w3_swiglu", SK_SWIGLU_HILO, w.xhl, TD, d.D, 1, lw->w1, lw->w3, nullptr, 0, 0, 2 * d.F,
+                     d.D, 1, w.uhl, (int64_t)T * d.F))
+    return e;
+  // a10: h += u w2^T (partials folded in place; w == nullptr: no normalisation)
+  if (int e = skinny("skinny_w2", SK_PARTIAL, w.uhl, (int64_t)T * d.F, d.F, 1, lw->w2, nullptr, nullptr, 0, 0, d.D,
+                     d.F, w.ks3, w.w2_part, TD))
+    return e;
+  return rmsnorm(d, 0, h, 0, d.D, w.w2_part, w.ks3, TD, nullptr, a->norm_eps, h, 0, T, s);
+}
+
 // One prefill layer.  h [T][D] fp32 is updated in place (h == y after the
 // copy-free residual epilogues); x_in is the layer input (may equal h).
 int run_layer_prefill(const llama_args *a, const Dims &d, const llama_layer_w *lw, const float *x_in, float *h,
@@ -361,6 +472,8 @@ int run_layer_prefill(const llama_args *a, const Dims &d, const llama_layer_w *l
   void *kc = kv ? kv->k : w.k;
   void *vc = kv ? kv->v : w.v;
   if (!table_ready) LAUNCH("rope_table", launch_rope_table(w.tab, nullptr, start_pos, INT32_MAX, S, d.hd, a->rope_theta, s));
+  if (d.dt == LLAMA_BF16 && T <= kSkinnyRows)
+    return run_layer_prefill_skinny(a, d, lw, x_in, h, B, S, start_pos, kc, vc, cap, w, kv_lo, s);
 
   if (d.dt == LLAMA_BF16) {
     // a2: attention_norm -> bf16

@@ -32,6 +32,7 @@ struct RopeQkvArgs {
   int cap;             // cache capacity (positions per sequence)
   float *qout;         // [rows][H*hd] fp32 (or nullptr)
   uint16_t *qhl;       // optional: q * qscale as bf16 hi/lo planes [2][rows][H*hd]
+  uint16_t *qbf;       // optional: q as bf16 [rows][H*hd] (prefill attention operand)
   float qscale;
   void *kc, *vc;       // [B][cap][G][hd] (dtype)
   float *knew, *vnew;  // optional: rotated k and v of each row in fp32, [rows][G*hd]

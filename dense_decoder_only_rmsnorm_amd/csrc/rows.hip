@@ -169,7 +169,8 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2 *__restrict__ ta
 // first) [P2 3.2 apply_rotary_emb, 3.3-3.4 cache write; P1 6.8-6.10].
 //   qkv row r = [q (H*hd) | k (G*hd) | v (G*hd)], sum over nsplit partials.
 //   q, k: adjacent pairs rotated by the table row of r; v copied.
-//   q -> qout[r][H*hd] (fp32); k, v -> cache[b][p][g][hd] (TC), where
+//   q -> qout[r][H*hd] (fp32), qbf (bf16) and/or qhl (scaled hi/lo planes);
+//   k, v -> cache[b][p][g][hd] (TC), where
 //   b = r / S, s = r % S and p = (pos ? clamp(pos[b]) : start_pos) + s.
 // One thread per pair.
 // ---------------------------------------------------------------------------
@@ -210,6 +211,8 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(RopeQkvArgs a) {
   }
   if (j < Hq) {
     if (a.qout) *reinterpret_cast<float2 *>(a.qout + (int64_t)r * Hq + j) = make_float2(x0, x1);
+    if (a.qbf)
+      *reinterpret_cast<uint32_t *>(a.qbf + (int64_t)r * Hq + j) = (uint32_t)f2bf(x0) | ((uint32_t)f2bf(x1) << 16);
     if (a.qhl) {
       u16 h0, l0, h1, l1;
       split_hilo(x0 * a.qscale, h0, l0);

@@ -42,14 +42,16 @@ constexpr int SK_KCH = 64;     // k per LDS stage
 constexpr int SK_STAGES = 2;
 constexpr int SK_ROWB = SK_KCH * 2;  // bytes per tile row (128)
 
-template <int NR, int MB, int EPI>
-__global__ __launch_bounds__(NR * 8) void skinny_kernel(SkinnyArgs a) {
-  constexpr int NT = NR * 8, NW = NT / 64;  // threads, waves
+template <int NR, int RW, int MB, int EPI>
+__global__ __launch_bounds__((NR / RW) * 128) void skinny_kernel(SkinnyArgs a) {
+  constexpr int NG = NR / RW;               // row groups of RW B-rows
+  constexpr int NW = 2 * NG, NT = NW * 64;  // waves (a row group and a 32-k half each), threads
+  constexpr int NB = RW / 16;               // 16-row MFMA blocks per wave
   // stage layout (bf16): A hi [64][64], A lo [64][64], B [NR][64]
   constexpr int ST_ELEMS = (128 + NR) * SK_KCH;
   extern __shared__ __align__(16) u16 sm[];  // [SK_STAGES][ST_ELEMS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wcol = wave % (NW / 2), khalf = wave / (NW / 2);
+  const int rg = wave % NG, khalf = wave / NG;
   const int nblk0 = blockIdx.x;
   const int ks = blockIdx.y;
   const int Kc = a.K / a.ksplit;
@@ -63,7 +65,8 @@ __global__ __launch_bounds__(NR * 8) void skinny_kernel(SkinnyArgs a) {
   // chunk L%8 holding logical chunk (L%8) ^ ((row >> 1) & 7).  Rows past M or
   // past the weight read a clamped valid row: they only feed outputs that are
   // never stored.
-  constexpr int NP = (16 + NR / 8) / NW;  // pieces per wave: 3 (NR 64), 2 (NR 128)
+  static_assert((16 + NR / 8) % NW == 0, "pieces spread evenly over the waves");
+  constexpr int NP = (16 + NR / 8) / NW;
   const int lr = lane >> 3, lq = lane & 7;
   const u16 *src[NP];
 #pragma unroll
@@ -109,6 +112,7 @@ __global__ __launch_bounds__(NR * 8) void skinny_kernel(SkinnyArgs a) {
       // activation rows from MB*16 on are never read by the MFMAs (few rows:
       // the prefill LM head, small decode batches): their pieces are skipped
       if (p < 16 && (p & 7) * 8 >= MB * 16) continue;
+      if (p >= 8 && p < 16 && !a.use_lo) continue;  // one activation plane: the lo pieces are never read
       u16 *dst = st + p * 8 * SK_KCH;
       __builtin_amdgcn_global_load_lds((const void *)(src[i] + chunk * SK_KCH),
                                        (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
@@ -118,9 +122,11 @@ __global__ __launch_bounds__(NR * 8) void skinny_kernel(SkinnyArgs a) {
   // fragment offsets: row (lane % 16) of a 16-row block, logical chunk 4*kk + lane/16
   const int frow = lane & 15;
   const int sw = (frow >> 1) & 7;
-  f32x4 acc[MB];
+  f32x4 acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   issue(0, 0);
   for (int ch = 0; ch < nchunk; ++ch) {
@@ -130,38 +136,50 @@ __global__ __launch_bounds__(NR * 8) void skinny_kernel(SkinnyArgs a) {
     asm volatile("s_barrier" ::: "memory");
     if (ch + 1 < nchunk) issue((ch + 1) % SK_STAGES, ch + 1);
     const u16 *st = sm + (ch % SK_STAGES) * ST_ELEMS;
-    const u16 *bp = st + 2 * 64 * SK_KCH + (wcol * 16 + frow) * SK_KCH;
-    {
-      const int kk = khalf;  // this wave's 32-k half of the stage
-      const int co = ((4 * kk + (lane >> 4)) ^ sw) * 8;
-      const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(bp + co);
+    // this wave's 32-k half of the stage, rows rg*RW + 16 j of B (the row
+    // swizzle is the same for every 16-row block)
+    const int co = ((4 * khalf + (lane >> 4)) ^ sw) * 8;
+    bf16x8 bb[NB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const u16 *ap = st + (mb * 16 + frow) * SK_KCH + co;
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(ap), bb, acc[mb], 0, 0, 0);
-        if (a.use_lo)
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(ap + 64 * SK_KCH), bb,
-                                                            acc[mb], 0, 0, 0);
+    for (int j = 0; j < NB; ++j)
+      bb[j] = *reinterpret_cast<const bf16x8 *>(st + 2 * 64 * SK_KCH + (rg * RW + j * 16 + frow) * SK_KCH + co);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const u16 *ap = st + (mb * 16 + frow) * SK_KCH + co;
+      const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(ap);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb[j], acc[mb][j], 0, 0, 0);
+      if (a.use_lo) {
+        const bf16x8 al = *reinterpret_cast<const bf16x8 *>(ap + 64 * SK_KCH);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb[j], acc[mb][j], 0, 0, 0);
       }
     }
   }
   __syncthreads();  // stages are reused for the epilogue
 
-  // wave pair (w, w + NW/2) holds column block wcol: acc[mb][r] = partial
-  // C[mb*16 + 4*(lane/16) + r][16*wcol + lane%16] over its k halves
+  // waves (rg, 0) and (rg, 1) hold B-rows rg*RW .. +RW-1 over the two k
+  // halves: acc[mb][j][r] = partial C[mb*16 + 4*(lane/16) + r][rg*RW + 16j + lane%16]
   float *red = reinterpret_cast<float *>(sm);  // [MB*16 rows][NR cols]
   if (khalf == 0) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[(mb * 16 + 4 * (lane >> 4) + r) * NR + wcol * 16 + frow] = acc[mb][r];
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          red[(mb * 16 + 4 * (lane >> 4) + r) * NR + rg * RW + j * 16 + frow] = acc[mb][j][r];
   }
   __syncthreads();
   if (khalf == 1) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[(mb * 16 + 4 * (lane >> 4) + r) * NR + wcol * 16 + frow] += acc[mb][r];
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          red[(mb * 16 + 4 * (lane >> 4) + r) * NR + rg * RW + j * 16 + frow] += acc[mb][j][r];
   }
   __syncthreads();
   constexpr int ROWS = MB * 16;
@@ -214,35 +232,35 @@ __global__ __launch_bounds__(NR * 8) void skinny_kernel(SkinnyArgs a) {
   }
 }
 
-template <int NR, int MB, int EPI>
+template <int NR, int RW, int MB, int EPI>
 hipError_t launch_one(const SkinnyArgs &a, dim3 grid, hipStream_t s) {
   // two stages; the epilogue's MB*16 x NR floats fit in the same space
   constexpr size_t lds = (size_t)SK_STAGES * (128 + NR) * SK_KCH * sizeof(u16);
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny_kernel<NR, MB, EPI>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&skinny_kernel<NR, RW, MB, EPI>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)lds);
   (void)attr;
-  hipLaunchKernelGGL((skinny_kernel<NR, MB, EPI>), grid, dim3(NR * 8), lds, s, a);
+  hipLaunchKernelGGL((skinny_kernel<NR, RW, MB, EPI>), grid, dim3((NR / RW) * 128), lds, s, a);
   return hipGetLastError();
 }
 
-template <int NR, int MB>
-hipError_t launch_mb(int epi, const SkinnyArgs &a, hipStream_t s) {
-  dim3 grid(skinny_nblk(a.N, a.K, epi), a.ksplit);
+template <int NR, int RW, int MB>
+hipError_t launch_mb(int epi, const SkinnyArgs &a, dim3 grid, hipStream_t s) {
   switch (epi) {
-    case SK_PARTIAL: return launch_one<NR, MB, SK_PARTIAL>(a, grid, s);
-    case SK_SWIGLU_HILO: return launch_one<NR, MB, SK_SWIGLU_HILO>(a, grid, s);
-    case SK_LOGITS: return launch_one<NR, MB, SK_LOGITS>(a, grid, s);
+    case SK_PARTIAL: return launch_one<NR, RW, MB, SK_PARTIAL>(a, grid, s);
+    case SK_SWIGLU_HILO: return launch_one<NR, RW, MB, SK_SWIGLU_HILO>(a, grid, s);
+    case SK_LOGITS: return launch_one<NR, RW, MB, SK_LOGITS>(a, grid, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int NR>
-hipError_t launch_nr(int epi, const SkinnyArgs &a, hipStream_t s) {
+template <int NR, int RW>
+hipError_t launch_nr(int epi, const SkinnyArgs &a, dim3 grid, hipStream_t s) {
   switch ((a.M + 15) / 16) {
-    case 1: return launch_mb<NR, 1>(epi, a, s);
-    case 2: return launch_mb<NR, 2>(epi, a, s);
-    case 3: return launch_mb<NR, 3>(epi, a, s);
-    case 4: return launch_mb<NR, 4>(epi, a, s);
+    case 1: return launch_mb<NR, RW, 1>(epi, a, grid, s);
+    case 2: return launch_mb<NR, RW, 2>(epi, a, grid, s);
+    case 3: return launch_mb<NR, RW, 3>(epi, a, grid, s);
+    case 4: return launch_mb<NR, RW, 4>(epi, a, grid, s);
   }
   return hipErrorInvalidValue;
 }
@@ -270,7 +288,8 @@ int skinny_nblk(int N, int K, int epi) {
 int skinny_ksplit(int N, int K) { return ksplit_rule(skinny_nblk(N, K, SK_PARTIAL), K); }
 
 hipError_t launch_skinny(int epi, const SkinnyArgs &a, hipStream_t s) {
-  return skinny_rows(a.N, a.K, epi) == 128 ? launch_nr<128>(epi, a, s) : launch_nr<64>(epi, a, s);
+  const dim3 grid(skinny_nblk(a.N, a.K, epi), a.ksplit);
+  return skinny_rows(a.N, a.K, epi) == 128 ? launch_nr<128, 16>(epi, a, grid, s) : launch_nr<64, 16>(epi, a, grid, s);
 }
 
 }  // namespace llk

@@ -64,6 +64,76 @@ def test_layer_forward_small(dtype, D, H, G, S, B):
         assert_close(host(kv[1][b]), t["v"], tol, f"v cache seq {b}")
 
 
+# bf16 layers on at most 64 tokens take the skinny (weight-streaming) path
+FEW_TOKEN_CASES = [
+    (256, 4, 2, 17, 2),    # hd 64, n_rep 2, 34 tokens
+    (384, 4, 1, 64, 1),    # hd 96, n_rep 4, exactly 64 tokens
+    (1024, 8, 1, 9, 3),    # hd 128, n_rep 8
+    (512, 4, 4, 1, 5),     # hd 128, MHA, one token per sequence
+    (1152, 12, 3, 21, 1),  # hd 96, QKV of 1728 rows (ragged 128-row block)
+]
+
+
+@pytest.mark.parametrize("D,H,G,S,B", FEW_TOKEN_CASES)
+def test_layer_forward_few_tokens(D, H, G, S, B):
+    cfg = small_cfg("bf16", D, H, G, S, B)
+    say(f"case layer few tokens {cfg.key} S={S} B={B}")
+    dm = R.DeviceModel(cfg, with_head=False)
+    x = I.hidden_x(cfg)
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    cap = S + 3
+    kv = R.kv_caches(cfg, 1, B, cap)[0]
+    args = R.args_for(cfg, max_batch=B, max_seq=cap)
+    ws = R.workspace(args, B, S)
+    M.llama_layer_forward(args, dm.layers[0], xd, y, B, S, 0, kv=kv, ws=ws)
+    torch.cuda.synchronize()
+    ref = OR.layer(cfg, x, taps=True)
+    assert_close(host(y), ref["y"], BF16_TOL, "layer output")
+    for b in range(B):
+        t = ref["taps"][b]
+        assert_close(host(kv[0][b, :S]), t["k"], BF16_TOL, f"k cache (rotated) seq {b}")
+        assert_close(host(kv[1][b, :S]), t["v"], BF16_TOL, f"v cache seq {b}")
+    # in place (y aliases x), without a cache
+    M.llama_layer_forward(args, dm.layers[0], xd, xd, B, S, 0, kv=None, ws=ws)
+    torch.cuda.synchronize()
+    assert_close(host(xd), ref["y"], BF16_TOL, "layer output in place")
+
+
+def test_chunked_prefill_few_tokens_per_chunk():
+    # three chunks of 20, 12 and 1 positions for 2 sequences, each under 64 tokens
+    chunks = [20, 12, 1]
+    S = sum(chunks)
+    cfg = small_cfg("bf16", 512, 8, 2, S, 2)
+    say(f"case chunked prefill, few tokens per chunk {cfg.key}")
+    dm = R.DeviceModel(cfg, with_head=False)
+    x = I.hidden_x(cfg)
+    cap = 40
+    kv = R.kv_caches(cfg, 1, 2, cap)[0]
+    args = R.args_for(cfg, max_batch=2, max_seq=cap)
+    ws = R.workspace(args, 2, max(chunks))
+    outs, p0 = [], 0
+    for n in chunks:
+        xc = torch.from_numpy(np.ascontiguousarray(x[:, p0:p0 + n])).cuda()
+        yc = torch.empty_like(xc)
+        M.llama_layer_forward(args, dm.layers[0], xc, yc, 2, n, p0, kv=kv, ws=ws)
+        outs.append(yc)
+        p0 += n
+    torch.cuda.synchronize()
+    ref = OR.layer(cfg, x)["y"]
+    assert_close(np.concatenate([host(o) for o in outs], axis=1), ref, BF16_TOL, "chunked layer output")
+
+
+def test_prefill_small_stack_few_tokens():
+    cfg = I.CONFIGS["c2"].with_(batch=4, seq_len=16)
+    say("case prefill, small GQA stack, 4 x 16 tokens (skinny path)")
+    _, ids, hidden, logits, nid, _ = _run_prefill(cfg, kv_cap=24)
+    ref = OR.prefill(cfg, ids, all_hidden=True)
+    assert_close(host(hidden), ref["hidden"], BF16_TOL, "final hidden")
+    assert_close(host(logits), ref["logits"], BF16_TOL, "logits")
+    assert_argmax(nid.cpu().numpy(), ref["logits"], "argmax")
+
+
 def test_layer_forward_in_place_without_cache():
     cfg = small_cfg("bf16", 512, 8, 2, 96, 1)
     say(f"case layer in-place {cfg.key}")
