@@ -336,6 +336,7 @@ def bench_configs(M, I, R, np, torch, steps):
             M.llama_prefill(args, dm.struct, ids, B, S, kv=None, logits=logits, next_id=nid, ws=ws)
 
         ms = time_steps(run, steps, 3, torch)
+        kt = kernel_times(run, steps, M, torch)
         flop = cfg.n_layers * layer_flops(cfg, dm.F, B, S) + 2.0 * B * cfg.dim * cfg.vocab_size
         tf = flop / (ms / 1e3) / 1e12
         peak = PEAK_BF16_TFLOPS if cfg.bf16 else PEAK_FP32_TFLOPS
@@ -343,7 +344,9 @@ def bench_configs(M, I, R, np, torch, steps):
                                 f"vocab {cfg.vocab_size}, {cfg.dtype}; prefill {B} x {S} + LM head",
                     "ms": round(ms, 4), "tokens_per_s": round(B * S / (ms / 1e3), 1),
                     "roofline": {"bound": "mfma" if cfg.bf16 else "fp32", "achieved": round(tf, 2),
-                                 "unit": "TFLOP/s", "peak": peak, "frac": round(tf / peak, 4), "flop": flop}}
+                                 "unit": "TFLOP/s", "peak": peak, "frac": round(tf / peak, 4), "flop": flop},
+                    "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in
+                                            sorted(kt.items(), key=lambda kv: -kv[1]["ms_per_step"])}}
         log(f"{key}: {ms:.3f} ms, {B * S / (ms / 1e3):.0f} tokens/s, {tf:.1f} TFLOP/s")
         del dm, ws, logits
     for key in ("c3_s17", "c3_s2048"):

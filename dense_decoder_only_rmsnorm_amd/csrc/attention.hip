@@ -11,8 +11,8 @@
 //                 and its softmax statistics; the output is accumulated as
 //                 O^T = V^T P^T, which consumes P^T straight from the score
 //                 registers (V is staged transposed in LDS).
-// attn_fwd_f32    prefill for the fp32 configuration (fp32 FMA, one query
-//                 per thread).
+// attn_fwd_f32    prefill for the fp32 configuration (fp32 FMA, 32 queries of
+//                 one head per block, 64-key tiles in LDS).
 // attn_decode     one query per sequence over the KV cache, split into key
 //                 chunks (partial max / sum / output), then combined.
 #include <type_traits>
@@ -493,59 +493,121 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
 // Prefill, fp32 (one wave per block, one query per lane)
 // ---------------------------------------------------------------------------
 template <int HD>
-__global__ __launch_bounds__(64) void attn_fwd_f32(AttnArgs a) {
-  constexpr int KT = 32;
-  __shared__ float Ks[KT][HD];
-  __shared__ float Vs[KT][HD];
-  const int lane = threadIdx.x;
-  const int qblk = gridDim.x - 1 - blockIdx.x;
+__global__ __launch_bounds__(256) void attn_fwd_f32(AttnArgs a) {
+  // A block owns 32 query positions of one head; 64-key tiles of K and V go
+  // through LDS.  Thread (tr, tc) = (t / 16, t % 16) scores rows 2tr, 2tr+1
+  // against keys tc + 16j (j < 4) and accumulates output columns tc + 16c.
+  // Row statistics (max, sum) are reduced over the 16 lanes of a row group.
+  constexpr int QT = 32, KT = 64, NC = HD / 16;
+  __shared__ float Qs[QT][HD + 1];
+  __shared__ float Ks[KT][HD + 1];
+  __shared__ __align__(16) float Vs[KT][HD];
+  __shared__ float Ps[QT][KT + 1];
+  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+  const int qblk = gridDim.x - 1 - blockIdx.x;  // longest causal ranges first
   const int h = blockIdx.y, b = blockIdx.z;
-  const int n_rep = a.H / a.G;
-  const int g = h / n_rep;
-  const int s = qblk * 64 + lane;
-  const bool valid = s < a.S;
-  const int qp = a.start_pos + (valid ? s : a.S - 1);
-  const int qlo = a.kv_lo ? min(max(a.kv_lo[(int64_t)b * a.S + (valid ? s : a.S - 1)], 0), qp) : 0;
-  const float *qrow = static_cast<const float *>(a.q) + (int64_t)(b * a.S + (valid ? s : a.S - 1)) * a.q_stride + h * HD;
-  float q[HD], o[HD];
+  const int g = h / (a.H / a.G);
+  const float *Q = static_cast<const float *>(a.q);
+  for (int i = tid; i < QT * HD; i += 256) {
+    const int r = i / HD, d = i % HD;
+    const int s = min(qblk * QT + r, a.S - 1);
+    Qs[r][d] = Q[(int64_t)(b * a.S + s) * a.q_stride + h * HD + d];
+  }
+  int qp[2], qlo[2];
 #pragma unroll
-  for (int d = 0; d < HD; ++d) { q[d] = qrow[d]; o[d] = 0.f; }
-  float m = -INFINITY, l = 0.f;
-  const int kv_end = a.start_pos + min(a.S, (qblk + 1) * 64);
+  for (int i = 0; i < 2; ++i) {
+    const int s = min(qblk * QT + 2 * tr + i, a.S - 1);
+    qp[i] = a.start_pos + s;
+    qlo[i] = a.kv_lo ? min(max(a.kv_lo[(int64_t)b * a.S + s], 0), qp[i]) : 0;
+  }
+  float o[2][NC], m[2], l[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) o[i][c] = 0.f;
+  }
+  const int kv_end = a.start_pos + min(a.S, (qblk + 1) * QT);  // keys [0, kv_end)
   const float *Kg = static_cast<const float *>(a.k) + ((int64_t)b * a.kcap * a.G + g) * HD;
   const float *Vg = static_cast<const float *>(a.v) + ((int64_t)b * a.kcap * a.G + g) * HD;
   const int64_t kstride = (int64_t)a.G * HD;
   for (int k0 = 0; k0 < kv_end; k0 += KT) {
-    for (int i = lane; i < KT * HD; i += 64) {
-      const int key = i / HD, d = i % HD;
-      const bool in = k0 + key < kv_end;
-      Ks[key][d] = in ? Kg[(k0 + key) * kstride + d] : 0.f;
-      Vs[key][d] = in ? Vg[(k0 + key) * kstride + d] : 0.f;
+    __syncthreads();  // the previous tile's K, V and P are no longer read
+    for (int i = tid; i < KT * HD / 4; i += 256) {
+      const int key = i / (HD / 4), d = (i % (HD / 4)) * 4;
+      const int kk = min(k0 + key, kv_end - 1);  // rows past the end are masked
+      const float4 kv = *reinterpret_cast<const float4 *>(Kg + (int64_t)kk * kstride + d);
+      const float4 vv = *reinterpret_cast<const float4 *>(Vg + (int64_t)kk * kstride + d);
+      Ks[key][d] = kv.x; Ks[key][d + 1] = kv.y; Ks[key][d + 2] = kv.z; Ks[key][d + 3] = kv.w;
+      *reinterpret_cast<float4 *>(&Vs[key][d]) = vv;
     }
     __syncthreads();
-    for (int j = 0; j < KT; ++j) {
-      const int key = k0 + j;
-      if (key > qp) break;
-      if (key < qlo) continue;
-      float dot = 0.f;
+    float sc[2][4];
 #pragma unroll
-      for (int d = 0; d < HD; ++d) dot = fmaf(q[d], Ks[j][d], dot);
-      const float sc = dot * a.scale;
-      const float m_new = fmaxf(m, sc);
-      const float corr = expf(m - m_new);
-      const float p = expf(sc - m_new);
-      l = l * corr + p;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int d = 0; d < HD; ++d) o[d] = fmaf(p, Vs[j][d], o[d] * corr);
-      m = m_new;
+      for (int j = 0; j < 4; ++j) sc[i][j] = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < HD; ++d) {
+      const float q0 = Qs[2 * tr][d], q1 = Qs[2 * tr + 1][d];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float kv = Ks[tc + 16 * j][d];
+        sc[0][j] = fmaf(q0, kv, sc[0][j]);
+        sc[1][j] = fmaf(q1, kv, sc[1][j]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = k0 + tc + 16 * j;
+        const bool vis = key <= qp[i] && key >= qlo[i] && key < kv_end;
+        sc[i][j] = vis ? sc[i][j] * a.scale : -INFINITY;
+        tmax = fmaxf(tmax, sc[i][j]);
+      }
+#pragma unroll
+      for (int x = 8; x >= 1; x >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, x, kWave));
+      const float m_new = fmaxf(m[i], tmax);
+      // m_new stays -inf while every key so far is masked; 0 stands in for it
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = expf(m[i] - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = expf(sc[i][j] - m_use);
+        Ps[2 * tr + i][tc + 16 * j] = p;
+        rs += p;
+      }
+#pragma unroll
+      for (int x = 8; x >= 1; x >>= 1) rs += __shfl_xor(rs, x, kWave);
+      l[i] = l[i] * alpha + rs;
+      m[i] = m_new;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) o[i][c] *= alpha;
     }
     __syncthreads();
+#pragma unroll 4
+    for (int k = 0; k < KT; ++k) {
+      const float p0 = Ps[2 * tr][k], p1 = Ps[2 * tr + 1][k];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const float v = Vs[k][tc + 16 * c];
+        o[0][c] = fmaf(p0, v, o[0][c]);
+        o[1][c] = fmaf(p1, v, o[1][c]);
+      }
+    }
   }
-  if (valid) {
-    float *orow = static_cast<float *>(a.o) + (int64_t)(b * a.S + s) * a.q_stride + h * HD;
-    const float inv = 1.0f / l;
 #pragma unroll
-    for (int d = 0; d < HD; ++d) orow[d] = o[d] * inv;
+  for (int i = 0; i < 2; ++i) {
+    const int s = qblk * QT + 2 * tr + i;
+    if (s >= a.S) continue;
+    float *orow = static_cast<float *>(a.o) + (int64_t)(b * a.S + s) * a.q_stride + h * HD;
+    const float inv = 1.0f / l[i];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) orow[tc + 16 * c] = o[i][c] * inv;
   }
 }
 
@@ -1090,8 +1152,8 @@ hipError_t prefill_hd(int dtype, const AttnArgs &a, hipStream_t s) {
     dim3 grid((a.S + QB - 1) / QB, a.G, a.B);
     hipLaunchKernelGGL(attn_fwd_bf16<HD>, grid, dim3(256), 0, s, a);
   } else {
-    dim3 grid((a.S + 63) / 64, a.H, a.B);
-    hipLaunchKernelGGL(attn_fwd_f32<HD>, grid, dim3(64), 0, s, a);
+    dim3 grid((a.S + 31) / 32, a.H, a.B);
+    hipLaunchKernelGGL(attn_fwd_f32<HD>, grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

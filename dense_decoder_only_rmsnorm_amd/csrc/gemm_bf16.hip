@@ -436,50 +436,79 @@ hipError_t launch_gemm_bf16(int epi, const GemmArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 GEMM for the fp32 configuration: C = A * B^T (+R).  64x64 tiles,
-// 16-deep K steps staged through LDS, 4x4 outputs per thread, fp32 FMA.
+// fp32 GEMM for the fp32 configuration: C = A * B^T (+R), A [M][K] and B [N][K]
+// row-major fp32, K a multiple of 64.  fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32: lane l supplies A[l % 32][l / 32] and
+// B^T[l / 32][l % 32]; output register r of lane l holds row
+// 8*(r/4) + 4*(l/32) + r%4, column l % 32).  A block of 256 threads owns a
+// 64 x 64 tile, each wave 32 x 32; K steps by 64 through LDS (rows padded to
+// 66 floats: the 32 rows x 2 k a fragment read touches fall in distinct
+// banks), the next step's operands (four 16-byte loads per matrix and
+// thread) prefetched into registers; even and odd k pairs accumulate in
+// separate chains so consecutive MFMAs are independent.  Rows past M or N
+// read a clamped valid row and are not stored.
 // ---------------------------------------------------------------------------
 namespace {
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__ A, const float *__restrict__ B,
                                                        float *C, int64_t ldc, const float *R, int64_t ldr, int M,
                                                        int N, int K) {
-  __shared__ float As[16][64 + 4];
-  __shared__ float Bs[16][64 + 4];
-  const int tid = threadIdx.x;
+  constexpr int BKF = 64, LD = BKF + 2, NL = 64 * BKF / 4 / 256;  // 16-byte loads per matrix and thread
+  __shared__ float As[64 * LD];
+  __shared__ float Bs[64 * LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
-  const int tr = tid / 16, tc = tid % 16;  // 16x16 threads, 4x4 outputs each
-  float acc[4][4] = {};
-  const int lr = tid / 4, lk = (tid % 4) * 4;  // loader: row lr (0..63), k lk..lk+3
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    float4 av = make_float4(0, 0, 0, 0), bv = make_float4(0, 0, 0, 0);
-    if (m0 + lr < M) av = *reinterpret_cast<const float4 *>(A + (int64_t)(m0 + lr) * K + k0 + lk);
-    if (n0 + lr < N) bv = *reinterpret_cast<const float4 *>(B + (int64_t)(n0 + lr) * K + k0 + lk);
-    As[lk + 0][lr] = av.x; As[lk + 1][lr] = av.y; As[lk + 2][lr] = av.z; As[lk + 3][lr] = av.w;
-    Bs[lk + 0][lr] = bv.x; Bs[lk + 1][lr] = bv.y; Bs[lk + 2][lr] = bv.z; Bs[lk + 3][lr] = bv.w;
-    __syncthreads();
+  // loader: load i of thread t covers row (t + 256 i) / 16, k 4 * (t % 16) .. +3
+  const int lk = (tid & 15) * 4;
+  const float *ap[NL], *bp[NL];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float a4[4], b4[4];
+  for (int i = 0; i < NL; ++i) {
+    const int r = (tid + 256 * i) >> 4;
+    ap[i] = A + (int64_t)min(m0 + r, M - 1) * K + lk;
+    bp[i] = B + (int64_t)min(n0 + r, N - 1) * K + lk;
+  }
+  f32x16 acc0, acc1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a4[i] = As[kk][tr * 4 + i];
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+  float4 ra[NL], rb[NL];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b4[j] = Bs[kk][tc * 4 + j];
+  for (int i = 0; i < NL; ++i) {
+    ra[i] = *reinterpret_cast<const float4 *>(ap[i]);
+    rb[i] = *reinterpret_cast<const float4 *>(bp[i]);
+  }
+  const int fr = lane & 31, fk = lane >> 5;
+  const float *af = As + (wm * 32 + fr) * LD + fk;
+  const float *bf = Bs + (wn * 32 + fr) * LD + fk;
+  for (int k0 = 0; k0 < K; k0 += BKF) {
+    __syncthreads();  // every wave is done with the previous step's tiles
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a4[i], b4[j], acc[i][j]);
+    for (int i = 0; i < NL; ++i) {
+      const int o = ((tid + 256 * i) >> 4) * LD + lk;
+      *reinterpret_cast<float2 *>(As + o) = make_float2(ra[i].x, ra[i].y);
+      *reinterpret_cast<float2 *>(As + o + 2) = make_float2(ra[i].z, ra[i].w);
+      *reinterpret_cast<float2 *>(Bs + o) = make_float2(rb[i].x, rb[i].y);
+      *reinterpret_cast<float2 *>(Bs + o + 2) = make_float2(rb[i].z, rb[i].w);
     }
     __syncthreads();
+    if (k0 + BKF < K) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        ra[i] = *reinterpret_cast<const float4 *>(ap[i] + k0 + BKF);
+        rb[i] = *reinterpret_cast<const float4 *>(bp[i] + k0 + BKF);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < BKF; kk += 4) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(af[kk], bf[kk], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(af[kk + 2], bf[kk + 2], acc1, 0, 0, 0);
+    }
   }
+  const int col = n0 + wn * 32 + fr;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + tr * 4 + i;
-    if (row >= M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + tc * 4 + j;
-      if (col >= N) continue;
-      const float v = acc[i][j];
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + wm * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+    if (row < M && col < N) {
+      const float v = acc0[r] + acc1[r];
       C[(int64_t)row * ldc + col] = R ? R[(int64_t)row * ldr + col] + v : v;
     }
   }
@@ -488,6 +517,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
 
 hipError_t launch_gemm_f32(int epi, const float *A, const float *B, float *C, int64_t ldc, const float *R,
                            int64_t ldr, int M, int N, int K, hipStream_t s) {
+  if (K % 64) return hipErrorInvalidValue;
   dim3 grid((M + 63) / 64, (N + 63) / 64);
   hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, A, B, C, ldc, epi == EPI_RESID ? R : nullptr, ldr, M, N,
                      K);

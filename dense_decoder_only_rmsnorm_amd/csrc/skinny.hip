@@ -20,7 +20,7 @@
 // than a deeper pipeline per block, keep enough loads in flight.  The
 // activation pieces are two thirds of a 64-row stage; 128-row blocks halve
 // that share, which pays wherever it still leaves enough blocks (the LM head,
-// and split-K products whose K slices stay at 512 or more).
+// and split-K products whose K slices stay at 256 or more).
 // MFMA 16x16x32 (v_mfma_f32_16x16x32_bf16): lane l supplies row/column
 // (l % 16) and eight consecutive k at 8*(l / 16); output register r of lane
 // l holds row 4*(l/16) + r, column l % 16.
@@ -39,17 +39,28 @@ namespace llk {
 namespace {
 
 constexpr int SK_KCH = 64;     // k per LDS stage
-constexpr int SK_STAGES = 2;
 constexpr int SK_ROWB = SK_KCH * 2;  // bytes per tile row (128)
 
-template <int NR, int RW, int MB, int EPI>
+// s_waitcnt vmcnt(n) for a wave-uniform n <= 15 (the count must be an immediate)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define LLK_VM(i) \
+  case i: __builtin_amdgcn_s_waitcnt(0x0F70 | i); break;
+    LLK_VM(0) LLK_VM(1) LLK_VM(2) LLK_VM(3) LLK_VM(4) LLK_VM(5) LLK_VM(6) LLK_VM(7)
+    LLK_VM(8) LLK_VM(9) LLK_VM(10) LLK_VM(11) LLK_VM(12) LLK_VM(13) LLK_VM(14)
+#undef LLK_VM
+    default: __builtin_amdgcn_s_waitcnt(0x0F70 | 15); break;
+  }
+}
+
+template <int NR, int RW, int NS, int MB, int EPI>
 __global__ __launch_bounds__((NR / RW) * 128) void skinny_kernel(SkinnyArgs a) {
   constexpr int NG = NR / RW;               // row groups of RW B-rows
   constexpr int NW = 2 * NG, NT = NW * 64;  // waves (a row group and a 32-k half each), threads
   constexpr int NB = RW / 16;               // 16-row MFMA blocks per wave
   // stage layout (bf16): A hi [64][64], A lo [64][64], B [NR][64]
   constexpr int ST_ELEMS = (128 + NR) * SK_KCH;
-  extern __shared__ __align__(16) u16 sm[];  // [SK_STAGES][ST_ELEMS]
+  extern __shared__ __align__(16) u16 sm[];  // [NS][ST_ELEMS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rg = wave % NG, khalf = wave / NG;
   const int nblk0 = blockIdx.x;
@@ -128,14 +139,25 @@ __global__ __launch_bounds__((NR / RW) * 128) void skinny_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
+  // loads this wave issues per stage (the same for every stage)
+  int nper = 0;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int p = wave + NW * i;
+    nper += !((p < 16 && (p & 7) * 8 >= MB * 16) || (p >= 8 && p < 16 && !a.use_lo));
+  }
+  // NS stages: chunks ch+1 .. ch+NS-1 are in flight while chunk ch is computed
+#pragma unroll
+  for (int c = 0; c < NS - 1; ++c)
+    if (c < nchunk) issue(c, c);
   for (int ch = 0; ch < nchunk; ++ch) {
-    // this wave's pieces of stage ch have landed; after the barrier every
+    // this wave's pieces of stage ch have landed (loads complete in order;
+    // the later chunks' pieces may stay in flight); after the barrier every
     // wave's have, and every wave is done reading the stage refilled next
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    wait_vmcnt(nper * max(0, min(NS - 2, nchunk - 1 - ch)));
     asm volatile("s_barrier" ::: "memory");
-    if (ch + 1 < nchunk) issue((ch + 1) % SK_STAGES, ch + 1);
-    const u16 *st = sm + (ch % SK_STAGES) * ST_ELEMS;
+    if (ch + NS - 1 < nchunk) issue((ch + NS - 1) % NS, ch + NS - 1);
+    const u16 *st = sm + (ch % NS) * ST_ELEMS;
     // this wave's 32-k half of the stage, rows rg*RW + 16 j of B (the row
     // swizzle is the same for every 16-row block)
     const int co = ((4 * khalf + (lane >> 4)) ^ sw) * 8;
@@ -232,35 +254,35 @@ __global__ __launch_bounds__((NR / RW) * 128) void skinny_kernel(SkinnyArgs a) {
   }
 }
 
-template <int NR, int RW, int MB, int EPI>
+template <int NR, int RW, int NS, int MB, int EPI>
 hipError_t launch_one(const SkinnyArgs &a, dim3 grid, hipStream_t s) {
-  // two stages; the epilogue's MB*16 x NR floats fit in the same space
-  constexpr size_t lds = (size_t)SK_STAGES * (128 + NR) * SK_KCH * sizeof(u16);
+  // NS stages; the epilogue's MB*16 x NR floats fit in the same space
+  constexpr size_t lds = (size_t)NS * (128 + NR) * SK_KCH * sizeof(u16);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&skinny_kernel<NR, RW, MB, EPI>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      reinterpret_cast<const void *>(&skinny_kernel<NR, RW, NS, MB, EPI>), hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)lds);
   (void)attr;
-  hipLaunchKernelGGL((skinny_kernel<NR, RW, MB, EPI>), grid, dim3((NR / RW) * 128), lds, s, a);
+  hipLaunchKernelGGL((skinny_kernel<NR, RW, NS, MB, EPI>), grid, dim3((NR / RW) * 128), lds, s, a);
   return hipGetLastError();
 }
 
-template <int NR, int RW, int MB>
+template <int NR, int RW, int NS, int MB>
 hipError_t launch_mb(int epi, const SkinnyArgs &a, dim3 grid, hipStream_t s) {
   switch (epi) {
-    case SK_PARTIAL: return launch_one<NR, RW, MB, SK_PARTIAL>(a, grid, s);
-    case SK_SWIGLU_HILO: return launch_one<NR, RW, MB, SK_SWIGLU_HILO>(a, grid, s);
-    case SK_LOGITS: return launch_one<NR, RW, MB, SK_LOGITS>(a, grid, s);
+    case SK_PARTIAL: return launch_one<NR, RW, NS, MB, SK_PARTIAL>(a, grid, s);
+    case SK_SWIGLU_HILO: return launch_one<NR, RW, NS, MB, SK_SWIGLU_HILO>(a, grid, s);
+    case SK_LOGITS: return launch_one<NR, RW, NS, MB, SK_LOGITS>(a, grid, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int NR, int RW>
+template <int NR, int RW, int NS = 2>
 hipError_t launch_nr(int epi, const SkinnyArgs &a, dim3 grid, hipStream_t s) {
   switch ((a.M + 15) / 16) {
-    case 1: return launch_mb<NR, RW, 1>(epi, a, grid, s);
-    case 2: return launch_mb<NR, RW, 2>(epi, a, grid, s);
-    case 3: return launch_mb<NR, RW, 3>(epi, a, grid, s);
-    case 4: return launch_mb<NR, RW, 4>(epi, a, grid, s);
+    case 1: return launch_mb<NR, RW, NS, 1>(epi, a, grid, s);
+    case 2: return launch_mb<NR, RW, NS, 2>(epi, a, grid, s);
+    case 3: return launch_mb<NR, RW, NS, 3>(epi, a, grid, s);
+    case 4: return launch_mb<NR, RW, NS, 4>(epi, a, grid, s);
   }
   return hipErrorInvalidValue;
 }
@@ -272,24 +294,47 @@ int ksplit_rule(int nblk, int K) {
   while (nblk * ks < 384 && ks < 16 && K % (ks * 2 * 128) == 0) ks *= 2;
   return ks;
 }
+
+// Launch plan of one product: rows per block, rows per wave, LDS stages and
+// K slices.  Measured at 64 activation rows on the 8B decode shapes with the
+// weights rotating beyond the Infinity Cache: one block of 128 rows per
+// compute unit with four stages in flight (three chunks loading while one is
+// computed) streams fastest when the blocks fill one round of the chip
+// (w1/w3 70 -> 58.5 us, w2 30.9 -> 27.8 us, wo 14.5 -> 12.5 us); products
+// with more row blocks than that keep two stages and about 1.5 blocks per
+// compute unit, as does the LM head (1002 blocks).
+struct Plan {
+  int nr, rw, ns, ks;
+};
+
+Plan skinny_plan(int N, int K, int epi) {
+  if (epi == SK_LOGITS) return {128, 16, 2, 1};
+  if (epi == SK_SWIGLU_HILO) return {128, 32, 4, 1};
+  const int nb = (N + 127) / 128;
+  int ks = 1;
+  while (nb * ks * 2 <= 256 && K % (ks * 2 * SK_KCH) == 0 && K / (ks * 2) >= 256) ks *= 2;
+  if (nb * ks >= 192) return {128, 32, 4, ks};
+  const int nr = K / ksplit_rule(nb, K) >= 256 ? 128 : 64;
+  return {nr, 16, 2, ksplit_rule((N + nr - 1) / nr, K)};
+}
 }  // namespace
 
-int skinny_rows(int N, int K, int epi) {
-  if (epi == SK_SWIGLU_HILO) return 64;  // 128 would leave CUs without a block
-  if (epi == SK_LOGITS) return 128;
-  return K / ksplit_rule((N + 127) / 128, K) >= 512 ? 128 : 64;
-}
+int skinny_rows(int N, int K, int epi) { return skinny_plan(N, K, epi).nr; }
 
 int skinny_nblk(int N, int K, int epi) {
   const int nr = skinny_rows(N, K, epi);
   return epi == SK_SWIGLU_HILO ? (N / 2 + nr / 2 - 1) / (nr / 2) : (N + nr - 1) / nr;
 }
 
-int skinny_ksplit(int N, int K) { return ksplit_rule(skinny_nblk(N, K, SK_PARTIAL), K); }
+int skinny_ksplit(int N, int K) { return skinny_plan(N, K, SK_PARTIAL).ks; }
 
 hipError_t launch_skinny(int epi, const SkinnyArgs &a, hipStream_t s) {
+  const Plan p = skinny_plan(a.N, a.K, epi);
+  if (epi == SK_PARTIAL && a.ksplit != p.ks) return hipErrorInvalidValue;  // partial planes sized for p.ks
   const dim3 grid(skinny_nblk(a.N, a.K, epi), a.ksplit);
-  return skinny_rows(a.N, a.K, epi) == 128 ? launch_nr<128, 16>(epi, a, grid, s) : launch_nr<64, 16>(epi, a, grid, s);
+  if (p.nr == 128 && p.rw == 32 && p.ns == 4) return launch_nr<128, 32, 4>(epi, a, grid, s);
+  if (p.nr == 128) return launch_nr<128, 16, 2>(epi, a, grid, s);
+  return launch_nr<64, 16, 2>(epi, a, grid, s);
 }
 
 }  // namespace llk
