@@ -1,0 +1,113 @@
+#!/usr/bin/env python3
+"""How far a stack of bf16 layers drifts from the exact result, by emulation.
+
+TEST INFRASTRUCTURE (an analysis script; pytest does not collect it).  It
+derives the comparison bar the multi-layer bf16 parity tests use.  It runs
+the 8B-shaped prefill (seeded weights and token ids, the first S positions)
+twice: through the fp64 oracle, and through a float32 numpy emulation of the
+GPU path's number handling -- fp32 arithmetic and residual stream, with bf16
+rounding exactly where the GPU kernels round: the normalized activations
+that feed the projections, q, the keys and values stored in the bf16 cache
+[P2 "Build your own Llama 3" 3.3: the cache holds the activation type], the
+attention probabilities fed to P.V, the attention output and the SwiGLU
+product.  It prints, after every few layers, max|emulated - exact| /
+max|exact| over all rows, and at the end the same ratio for the last row's
+logits, for the full emulation and for variants that skip some roundings.
+
+Findings at S = 512 (the GPU at S = 8192 agrees: 6.8e-3 after one layer,
+2.1e-2 after eight): the ratio grows like sqrt(L), from 8.6e-3 after one layer
+to 2.1e-2 after 8 and 4.3e-2 after 32 (logits 4.3e-2); with every rounding
+removed except the bf16 K/V cache it still reaches 2.0e-2 after 32 layers.
+So a bf16 stack meets max-abs <= 2e-2 max|ref| up to about four layers, and
+the bar for L layers is taken as 2e-2 * max(1, sqrt(L / 4)).
+
+Usage: python tests/bf16_drift_model.py [S] [layers]
+"""
+from __future__ import annotations
+
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import inputs as I  # noqa: E402
+from oracle import llama as OL  # noqa: E402
+from oracle import runner as OR  # noqa: E402
+
+ALL = frozenset({"xn", "q", "k", "v", "p", "o", "u"})
+
+
+def bf16(x):
+    return I.bf16_bits_to_f32(I.f32_to_bf16_bits(np.asarray(x, np.float32)))
+
+
+def rope_f32(x, pos, hd, theta):
+    """Rotation of adjacent pairs with an fp32 cos/sin table built from fp64 angles."""
+    i = np.arange(hd // 2, dtype=np.float64)
+    ang = np.outer(pos.astype(np.float64), 1.0 / (theta ** (2 * i / hd)))
+    c, s = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    a0, a1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = a0 * c[:, None, :] - a1 * s[:, None, :]
+    out[..., 1::2] = a0 * s[:, None, :] + a1 * c[:, None, :]
+    return out
+
+
+def layer_emulated(h, lw, args, rounded):
+    """One pre-norm block in float32 with bf16 rounding at the points in ``rounded``."""
+    r = (lambda name, x: bf16(x) if name in rounded else np.asarray(x, np.float32))
+    S = h.shape[0]
+    H, G, D = args["n_heads"], args["n_kv_heads"], args["dim"]
+    hd, rep = D // H, H // G
+    pos = np.arange(S)
+    xn = r("xn", h / np.sqrt(np.mean(h * h, -1, keepdims=True) + args["norm_eps"]) * lw["attention_norm"])
+    q = r("q", rope_f32((xn @ lw["wq"].T).reshape(S, H, hd), pos, hd, args["rope_theta"]))
+    k = r("k", rope_f32((xn @ lw["wk"].T).reshape(S, G, hd), pos, hd, args["rope_theta"]))
+    v = r("v", (xn @ lw["wv"].T).reshape(S, G, hd))
+    mask = np.triu(np.full((S, S), -np.inf, np.float32), 1)
+    o = np.empty((S, H, hd), np.float32)
+    for hh in range(H):
+        sc = q[:, hh] @ k[:, hh // rep].T / np.float32(np.sqrt(hd)) + mask
+        p = np.exp(sc - sc.max(-1, keepdims=True))
+        o[:, hh] = (r("p", p) @ v[:, hh // rep]) / p.sum(-1, keepdims=True)
+    h1 = h + r("o", o.reshape(S, H * hd)) @ lw["wo"].T
+    xn2 = r("xn", h1 / np.sqrt(np.mean(h1 * h1, -1, keepdims=True) + args["norm_eps"]) * lw["ffn_norm"])
+    g, up = xn2 @ lw["w1"].T, xn2 @ lw["w3"].T
+    return h1 + r("u", g / (1 + np.exp(-g)) * up) @ lw["w2"].T
+
+
+def main():
+    S = int(sys.argv[1]) if len(sys.argv) > 1 else 512
+    L = int(sys.argv[2]) if len(sys.argv) > 2 else 32
+    cfg = I.CONFIGS["c4"]
+    m = OR.model_of(cfg)
+    a = OR.args_of(cfg)
+    ids = I.prompt_ids(cfg)[0][:S]
+    variants = {"gpu": ALL, "kv cache only": frozenset({"k", "v"}), "none": frozenset()}
+    emb = m.rows("tok_embeddings", ids)
+    h64 = emb.astype(np.float64)
+    hs = {k: emb.astype(np.float32) for k in variants}
+    for l in range(L):
+        t0 = time.time()
+        lw = m.layer(l)
+        h64 = OL.layer_forward(h64, {k: v.astype(np.float64) for k, v in lw.items()}, a, np.arange(S))
+        for k, R in variants.items():
+            hs[k] = layer_emulated(hs[k], lw, a, R)
+        if l < 2 or (l + 1) % 4 == 0:
+            ratios = " ".join(f"{k}: {np.max(np.abs(hs[k] - h64)) / np.max(np.abs(h64)):.2e}" for k in variants)
+            print(f"after {l + 1} layers: {ratios} ({time.time() - t0:.0f} s)", flush=True)
+    ref = OL.lm_head(OL.rms_norm(h64[-1:], m.get("norm"), cfg.norm_eps), m.get("output"))
+    for k in variants:
+        lg = OL.lm_head(OL.rms_norm(hs[k][-1:].astype(np.float64), m.get("norm"), cfg.norm_eps), m.get("output"))
+        print(f"{k}: last-row logits {np.max(np.abs(lg - ref)) / np.max(np.abs(ref)):.2e}, argmax "
+              f"{int(OL.argmax_first(lg)[0])} (exact {int(OL.argmax_first(ref)[0])}, top-2 gap "
+              f"{float(OL.top2_gap(ref)[0]):.3f})", flush=True)
+
+
+if __name__ == "__main__":
+    main()
