@@ -9,14 +9,18 @@
 //
 // Tiling: a block of 256 threads (4 waves in a 2x2 grid) owns a BM x BN
 // output tile; each wave owns (BM/2) x (BN/2) as 32x32 MFMA blocks.  The K
-// loop steps by 64 through two LDS stages.  Tiles move global -> LDS with
-// global_load_lds_dwordx4 (no staging registers): one wave instruction fills
-// 1 KB = 8 tile rows of 128 bytes, lane L landing at 16-byte slot L.  Each
-// lane fetches the global piece that belongs in its slot under an XOR
-// swizzle (16-byte chunk c of row r lives at chunk c ^ ((r >> 1) & 7)), so
-// the 16-byte fragment reads of 16 consecutive rows hit 16 distinct bank
-// groups.  The next stage is loading while the MFMAs consume the current
-// one; operand fragments are double-buffered in registers across k-steps.
+// loop steps through chunks of BK = 32 or 64 held in NS LDS stages.  Tiles
+// move global -> LDS with global_load_lds_dwordx4 (no staging registers): one
+// wave instruction fills 1 KB = 1024 / (2 BK) tile rows, lane L landing at
+// 16-byte slot L.  Each lane fetches the global piece that belongs in its
+// slot under an XOR swizzle (16-byte chunk c of row r lives at chunk
+// c ^ ((r >> SH) & (BK/8 - 1)), SH = 1 for 128-byte rows and 2 for 64-byte
+// rows), so the 16-byte fragment reads of 16 consecutive rows hit 16
+// distinct bank groups.  While chunk kt is computed, chunks kt+1 .. kt+NS-1
+// are in flight or landed: the loads of a chunk are issued NS-1 chunks of
+// MFMA work before they are needed, which is what hides the latency of the
+// operands that miss L2.  Operand fragments are double-buffered in
+// registers across k-steps.
 //
 // MFMA 32x32x16 operand layout (lane l): A supplies row (l % 32) and eight
 // consecutive k at 8*(l / 32); B likewise for output column (l % 32).  Output
@@ -30,17 +34,34 @@
 namespace llk {
 
 namespace {
-constexpr int BK = 64;
+// s_waitcnt operand: vmcnt <= n (n < 64) and lgkmcnt = 0, expcnt not waited on
+constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
 
-template <int BM, int BN, int EPI>
+// One 1 KB load into LDS: lane L's 16 bytes at byte voff + soff of the raw
+// buffer [base, base + bytes) (clamped to 4 GiB - 1; reads past the end
+// return zero) land at LDS slot L of dst.
+__device__ __forceinline__ void buffer_load_lds16(const u16 *base, int64_t bytes, u16 *dst, uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16 *>(base), (short)0, (int)(uint32_t)(bytes < 0xFFFFFFFFll ? bytes : 0xFFFFFFFFll),
+      0x00020000);  // untyped, 32-bit data format, no stride
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
+}
+
+template <int BM, int BN, int BK, int NS, int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int RS = BK;                  // LDS row stride (bf16), 128 bytes, unpadded
-  constexpr int AI = BM / 32, BI = BN / 32;  // 8-row load instructions per wave (A, B)
+  constexpr int RS = BK;                     // LDS row stride (bf16): 64 or 128 bytes, unpadded
+  constexpr int CH = BK / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;               // tile rows one 1 KB load instruction fills
+  constexpr int SH = CH == 8 ? 1 : 2;        // swizzle shift
+  constexpr int AI = BM / RPI / 4, BI = BN / RPI / 4;  // load instructions per wave and stage (A, B)
+  constexpr int NL = AI + BI;
+  static_assert(BK == 32 || BK == 64, "rows of 64 or 128 bytes");
+  static_assert(NS >= 2 && NS * NL <= 63, "the outstanding loads of all stages fit the vmcnt counter");
   extern __shared__ __align__(16) u16 smem[];
-  u16 *As = smem;                         // [2][BM][RS]
-  u16 *Bs = smem + 2 * BM * RS;           // [2][BN][RS]
+  u16 *As = smem;                         // [NS][BM][RS]
+  u16 *Bs = smem + NS * BM * RS;          // [NS][BN][RS]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -63,66 +84,63 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const int n0 = bn * BN;
   const int K = a.K;
 
-  // Loader: wave w fills tile rows 8j..8j+7 for j = w*AI + i (A) and w*BI + i
-  // (B).  Lane L writes slot L of that 1 KB block: row 8j + L/8, physical
-  // chunk L%8, which holds logical chunk (L%8) ^ ((row >> 1) & 7).  Rows past
-  // M (A) or past the weight's rows (B) read a clamped valid row: they only
-  // feed outputs that are never stored.
-  const int lr = lane >> 3, lq = lane & 7;
-  const u16 *asrc[AI];
+  // Loader: wave w fills the RPI-row groups j = w*AI + i (A) and w*BI + i
+  // (B).  Lane L writes slot L of that 1 KB block: row RPI*j + L/CH,
+  // physical chunk L%CH, which holds logical chunk (L%CH) ^ swizzle(row).
+  // The loads are raw buffer loads: A's resource starts at the tile's first
+  // row, each weight matrix's covers the whole matrix (below 4 GiB, checked
+  // at launch); a lane's 32-bit offset is its row times the row pitch plus
+  // its 16-byte chunk, and the k position of the chunk goes in the scalar
+  // offset, so a refill costs no vector address arithmetic.  Rows past M
+  // (A) or past a weight's rows (B) read a clamped valid row: they only feed
+  // outputs that are never stored.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int lr = lane / CH, lq = lane % CH;
+  const u16 *abase = a.A + (int64_t)m0 * a.lda;
+  const int64_t abytes = (int64_t)(a.M - m0) * a.lda * 2;
+  uint32_t aoff[AI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int t = (wave * AI + i) * 8 + lr;
-    const int c = lq ^ ((t >> 1) & 7);
-    asrc[i] = a.A + (int64_t)min(m0 + t, a.M - 1) * a.lda + c * 8;
+    const int t = (wave * AI + i) * RPI + lr;
+    const int c = lq ^ ((t >> SH) & (CH - 1));
+    aoff[i] = (uint32_t)((min(m0 + t, a.M - 1) - m0) * a.lda * 2 + c * 16);
   }
-  const u16 *bsrc[BI];
+  // weight matrices: B0 alone, w1 / w3 (SwiGLU), or wq / wk / wv (QKV)
+  const int nq = EPI == EPI_QKV_ROPE ? a.nq : (EPI == EPI_SWIGLU ? a.N / 2 : a.N);
+  const int nk = EPI == EPI_QKV_ROPE ? a.nk : (EPI == EPI_SWIGLU ? a.N / 2 : 0);
+  uint32_t boff[BI];
+  int bsel[BI];  // which matrix load i reads (uniform: a row group never straddles two)
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    const int t = (wave * BI + i) * 8 + lr;
-    const int c = lq ^ ((t >> 1) & 7);
-    const u16 *base;
+    const int t = (wave * BI + i) * RPI + lr;
+    const int tg = (wv * BI + i) * RPI;  // the group's first tile row
+    const int c = lq ^ ((t >> SH) & (CH - 1));
     int wr, nrows;
     if (EPI == EPI_SWIGLU) {
       wr = n0 / 2 + (t >> 6) * 32 + (t & 31);  // 64 tile rows = 32 gate rows (w1) + 32 up rows (w3)
-      base = ((t >> 5) & 1) ? a.B1 : a.B0;
+      bsel[i] = (tg >> 5) & 1;
       nrows = a.N / 2;
     } else if (EPI == EPI_QKV_ROPE) {
-      const int n = n0 + t;
-      base = n < a.nq ? a.B0 : (n < a.nq + a.nk ? a.B1 : a.B2);
+      const int n = n0 + t, ng = n0 + tg;
+      bsel[i] = ng < a.nq ? 0 : (ng < a.nq + a.nk ? 1 : 2);
       wr = n < a.nq ? n : (n < a.nq + a.nk ? n - a.nq : n - a.nq - a.nk);
       nrows = n < a.nq ? a.nq : (n < a.nq + a.nk ? a.nk : a.N - a.nq - a.nk);
     } else {
       wr = n0 + t;
-      base = a.B0;
+      bsel[i] = 0;
       nrows = a.N;
     }
-    bsrc[i] = base + (int64_t)min(wr, nrows - 1) * a.ldb + c * 8;
+    boff[i] = (uint32_t)(min(wr, nrows - 1) * a.ldb * 2 + c * 16);
   }
   // one load instruction of a stage refill: l < AI for A, then B
   auto issue_one = [&](int stage, int k0, int l) {
     if (l < AI) {
-      const int j = __builtin_amdgcn_readfirstlane(wave * AI + l);
-      __builtin_amdgcn_global_load_lds((const void *)(asrc[l] + k0),
-                                       (__attribute__((address_space(3))) void *)(As + stage * BM * RS + j * 8 * RS), 16, 0, 0);
+      buffer_load_lds16(abase, abytes, As + stage * BM * RS + (wv * AI + l) * RPI * RS, aoff[l], k0 * 2);
     } else {
-      const int j = __builtin_amdgcn_readfirstlane(wave * BI + (l - AI));
-      __builtin_amdgcn_global_load_lds((const void *)(bsrc[l - AI] + k0),
-                                       (__attribute__((address_space(3))) void *)(Bs + stage * BN * RS + j * 8 * RS), 16, 0, 0);
-    }
-  };
-  auto issue = [&](int stage, int k0) {
-    u16 *ad = As + stage * BM * RS;
-    u16 *bd = Bs + stage * BN * RS;
-#pragma unroll
-    for (int i = 0; i < AI; ++i) {
-      const int j = __builtin_amdgcn_readfirstlane(wave * AI + i);
-      __builtin_amdgcn_global_load_lds((const void *)(asrc[i] + k0), (__attribute__((address_space(3))) void *)(ad + j * 8 * RS), 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < BI; ++i) {
-      const int j = __builtin_amdgcn_readfirstlane(wave * BI + i);
-      __builtin_amdgcn_global_load_lds((const void *)(bsrc[i] + k0), (__attribute__((address_space(3))) void *)(bd + j * 8 * RS), 16, 0, 0);
+      const int i = l - AI;
+      const u16 *bb = bsel[i] == 0 ? a.B0 : (bsel[i] == 1 ? a.B1 : a.B2);
+      const int rows = bsel[i] == 0 ? nq : (bsel[i] == 1 ? nk : a.N - nq - nk);
+      buffer_load_lds16(bb, (int64_t)rows * a.ldb * 2, Bs + stage * BN * RS + (wv * BI + i) * RPI * RS, boff[i], k0 * 2);
     }
   };
 
@@ -135,25 +153,33 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // fragment read offsets: row (lane & 31) of a 32-row block, logical chunk
-  // 2*kk + (lane >> 5), swizzled with ((row >> 1) & 7)
+  // 2*kk + (lane >> 5), swizzled
   const int frow = lane & 31;
-  const int sw = (frow >> 1) & 7;
+  const int sw = (frow >> SH) & (CH - 1);
   int koff[BK / 16];
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) koff[kk] = (((2 * kk + (lane >> 5)) ^ sw) * 8);
 
-  // Two stages.  Chunk kt is computed from stage kt&1 in four k-steps; the
-  // fragments of step kk+1 are read during the MFMAs of step kk.  In the last
-  // step of a chunk the wave waits for its loads of chunk kt+1, meets the
-  // others at the barrier, and then refills the stage it just finished with
-  // chunk kt+2 while it runs the step's remaining MFMAs: the refill loads and
-  // the first fragment reads of chunk kt+1 are spread between those MFMAs, so
-  // the address unit drains them while the matrix core stays busy.
+  // Chunk kt is computed from stage kt % NS in BK/16 k-steps; the fragments
+  // of step kk+1 are read during the MFMAs of step kk.  In the last step of a
+  // chunk the wave waits until its own loads of chunk kt+1 have landed (loads
+  // complete in order; those of chunks kt+2 .. kt+NS-1 stay in flight),
+  // meets the others at the barrier (after it every wave's part of chunk
+  // kt+1 is in LDS and every wave is done reading stage kt % NS), and then
+  // refills that stage with chunk kt+NS while it runs the step's remaining
+  // MFMAs: the refill loads and the first fragment reads of chunk kt+1 are
+  // spread between those MFMAs, so the address unit drains them while the
+  // matrix core stays busy.  Chunks past the last one load the last chunk
+  // again into a dead stage, which keeps the count of loads in flight, and
+  // so every wait, the same in every step.
   const int KT = K / BK;
   constexpr int KS = BK / 16;
-  issue(0, 0);
-  __syncthreads();
-  if (KT > 1) issue(1, BK);
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int l = 0; l < NL; ++l) issue_one(s, min(s, KT - 1) * BK, l);
+  __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((NS - 1) * NL));  // this wave's part of chunk 0 has landed
+  asm volatile("s_barrier" ::: "memory");                      // and everyone's
   bf16x8 af[2][FM], bfr[2][FN];
   {
     const u16 *Ab = As + (wm * WM + frow) * RS;
@@ -163,9 +189,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8 *>(Bb + j * 32 * RS + koff[0]);
   }
+  int cur = 0;  // stage of chunk kt
   auto run_chunk = [&](int kt, auto boundary) {
     constexpr bool BOUNDARY = decltype(boundary)::value;
-    const int cur = kt & 1;
+    const int nxt = cur + 1 == NS ? 0 : cur + 1;
     const u16 *Ab = As + (cur * BM + wm * WM + frow) * RS;
     const u16 *Bb = Bs + (cur * BN + wn * WN + frow) * RS;
 #pragma unroll
@@ -184,16 +211,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
           bfr[cb ^ 1][j] = *reinterpret_cast<const bf16x8 *>(Bb + j * 32 * RS + koff[kk + 1]);
         __builtin_amdgcn_sched_barrier(0);
       } else if (BOUNDARY) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of chunk kt+1 have landed
-        __syncthreads();                      // everyone's have, and everyone is done reading stage cur
-        // Refill (past the last chunk the last chunk is loaded again into
-        // this dead stage, which keeps the step free of branches), spread
-        // between the step's remaining MFMAs together with the first
-        // fragment reads of chunk kt+1.
-        const int k0 = min(kt + 2, KT - 1) * BK;
-        const u16 *An = As + ((cur ^ 1) * BM + wm * WM + frow) * RS;
-        const u16 *Bn = Bs + ((cur ^ 1) * BN + wn * WN + frow) * RS;
-        constexpr int NM = (FM - 1) * FN, NL = AI + BI, NR = FM + FN;
+        __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((NS - 2) * NL));
+        asm volatile("s_barrier" ::: "memory");
+        const int k0 = min(kt + NS, KT - 1) * BK;
+        const u16 *An = As + (nxt * BM + wm * WM + frow) * RS;
+        const u16 *Bn = Bs + (nxt * BN + wn * WN + frow) * RS;
+        constexpr int NM = (FM - 1) * FN, NR = FM + FN;
 #pragma unroll
         for (int q = 0; q < NM; ++q) {
           const int i = 1 + q / FN, j = q % FN;
@@ -217,10 +240,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    cur = nxt;
   };
   for (int kt = 0; kt + 1 < KT; ++kt) run_chunk(kt, std::true_type{});
   run_chunk(KT - 1, std::false_type{});
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // the refill of the dead stage has landed before LDS is reused
+  __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));  // the refills of dead stages have landed before LDS is reused
   __syncthreads();  // every wave is done with the stages before the epilogue reuses them
 
   // ---------------- epilogue ----------------
@@ -402,27 +426,30 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     *reinterpret_cast<uint4 *>(C + (int64_t)(m0 + rr) * a.ldc) = *reinterpret_cast<const uint4 *>(Cs + rr * LDC + c8);
 }
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int BK, int NS, int EPI>
 hipError_t launch_tile(const GemmArgs &a, hipStream_t s) {
   dim3 grid((a.M + BM - 1) / BM, (a.N + BN - 1) / BN);  // a.N counts B-rows
   constexpr int CN = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  const size_t lds = std::max((size_t)2 * (BM + BN) * BK * sizeof(u16), (size_t)BM * (CN + 8) * sizeof(u16));
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, EPI>),
+  const size_t lds = std::max((size_t)NS * (BM + BN) * BK * sizeof(u16), (size_t)BM * (CN + 8) * sizeof(u16));
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, BK, NS, EPI>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  (void)attr;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI>), grid, dim3(256), lds, s, a);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NS, EPI>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs &a, hipStream_t s) {
   const long tiles256 = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (tiles256 >= 512) return launch_tile<256, 256, EPI>(a, s);
-  return launch_tile<128, 128, EPI>(a, s);
+  if (tiles256 >= 512) return launch_tile<256, 256, 64, 2, EPI>(a, s);
+  return launch_tile<128, 128, 64, 2, EPI>(a, s);
 }
 }  // namespace
 
 hipError_t launch_gemm_bf16(int epi, const GemmArgs &a, hipStream_t s) {
+  // the loads take 32-bit byte offsets: every weight matrix and any 256 rows
+  // of the activations stay below 4 GiB
+  if ((int64_t)a.N * a.ldb * 2 > 0xFFFFFFFFll || (int64_t)256 * a.lda * 2 > 0xFFFFFFFFll) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_STORE_F32: return launch_epi<EPI_STORE_F32>(a, s);
     case EPI_RESID: return launch_epi<EPI_RESID>(a, s);
