@@ -109,28 +109,35 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const int nq = EPI == EPI_QKV_ROPE ? a.nq : (EPI == EPI_SWIGLU ? a.N / 2 : a.N);
   const int nk = EPI == EPI_QKV_ROPE ? a.nk : (EPI == EPI_SWIGLU ? a.N / 2 : 0);
   uint32_t boff[BI];
-  int bsel[BI];  // which matrix load i reads (uniform: a row group never straddles two)
+  const u16 *bbase[BI];  // the matrix load i reads (uniform: a row group never straddles two)
+  int64_t bbytes[BI];
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
     const int t = (wave * BI + i) * RPI + lr;
     const int tg = (wv * BI + i) * RPI;  // the group's first tile row
     const int c = lq ^ ((t >> SH) & (CH - 1));
-    int wr, nrows;
+    int wr, nrows, sel;
     if (EPI == EPI_SWIGLU) {
       wr = n0 / 2 + (t >> 6) * 32 + (t & 31);  // 64 tile rows = 32 gate rows (w1) + 32 up rows (w3)
-      bsel[i] = (tg >> 5) & 1;
+      sel = (tg >> 5) & 1;
       nrows = a.N / 2;
     } else if (EPI == EPI_QKV_ROPE) {
       const int n = n0 + t, ng = n0 + tg;
-      bsel[i] = ng < a.nq ? 0 : (ng < a.nq + a.nk ? 1 : 2);
+      sel = ng < a.nq ? 0 : (ng < a.nq + a.nk ? 1 : 2);
       wr = n < a.nq ? n : (n < a.nq + a.nk ? n - a.nq : n - a.nq - a.nk);
       nrows = n < a.nq ? a.nq : (n < a.nq + a.nk ? a.nk : a.N - a.nq - a.nk);
     } else {
       wr = n0 + t;
-      bsel[i] = 0;
+      sel = 0;
       nrows = a.N;
     }
     boff[i] = (uint32_t)(min(wr, nrows - 1) * a.ldb * 2 + c * 16);
+    // the matrix as an offset from B0 in arithmetic (a select between the
+    // pointer fields would become a scalar load of the argument block with a
+    // computed offset, and its wait, in every refill)
+    const int64_t d1 = a.B1 - a.B0, d2 = a.B2 - a.B0;
+    bbase[i] = a.B0 + (sel == 1 ? d1 : 0) + (sel == 2 ? d2 : 0);
+    bbytes[i] = (int64_t)(sel == 0 ? nq : (sel == 1 ? nk : a.N - nq - nk)) * a.ldb * 2;
   }
   // one load instruction of a stage refill: l < AI for A, then B
   auto issue_one = [&](int stage, int k0, int l) {
@@ -138,9 +145,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
       buffer_load_lds16(abase, abytes, As + stage * BM * RS + (wv * AI + l) * RPI * RS, aoff[l], k0 * 2);
     } else {
       const int i = l - AI;
-      const u16 *bb = bsel[i] == 0 ? a.B0 : (bsel[i] == 1 ? a.B1 : a.B2);
-      const int rows = bsel[i] == 0 ? nq : (bsel[i] == 1 ? nk : a.N - nq - nk);
-      buffer_load_lds16(bb, (int64_t)rows * a.ldb * 2, Bs + stage * BN * RS + (wv * BI + i) * RPI * RS, boff[i], k0 * 2);
+      buffer_load_lds16(bbase[i], bbytes[i], Bs + stage * BN * RS + (wv * BI + i) * RPI * RS, boff[i], k0 * 2);
     }
   };
 
