@@ -47,6 +47,18 @@ __device__ __forceinline__ void buffer_load_lds16(const u16 *base, int64_t bytes
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
 }
 
+// One float of the raw buffer [base, base + bytes) at byte voff + soff.
+__device__ __forceinline__ float buffer_load_f32(const float *base, int64_t bytes, uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(base), (short)0, (int)(uint32_t)(bytes < 0xFFFFFFFFll ? bytes : 0xFFFFFFFFll), 0x00020000);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buffer_store_f32(float v, float *base, int64_t bytes, uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      base, (short)0, (int)(uint32_t)(bytes < 0xFFFFFFFFll ? bytes : 0xFFFFFFFFll), 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+}
+
 template <int BM, int BN, int BK, int NS, int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WM = BM / 2, WN = BN / 2;
@@ -261,6 +273,38 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     // issued together from clamped, always valid addresses, so they overlap
     // instead of each waiting for the previous one; only stores are guarded.
     float *C = static_cast<float *>(a.C);
+    if (m0 + BM <= a.M && n0 + BN <= a.N) {
+      // A whole tile: raw buffer accesses from the tile's first element, the
+      // lane's column and row-within-group in a vector offset, the row of
+      // each accumulator register in the scalar offset; no guards and no
+      // per-element address arithmetic.
+      const int wmu = wv >> 1, wnu = wv & 1;
+      const float *Rt = a.R + (int64_t)m0 * a.ldr + n0;
+      float *Ct = C + (int64_t)m0 * a.ldc + n0;
+      const int64_t rbytes = ((int64_t)(a.M - m0) * a.ldr - n0) * 4, cbytes = ((int64_t)(a.M - m0) * a.ldc - n0) * 4;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        float rv[FN][16];
+        if (EPI == EPI_RESID) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const uint32_t vo = (uint32_t)((4 * (lane >> 5)) * a.ldr + wnu * WN + j * 32 + col_l) * 4u;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              rv[j][r] = buffer_load_f32(Rt, rbytes, vo, (uint32_t)((wmu * WM + i * 32 + 8 * (r / 4) + (r % 4)) * a.ldr) * 4u);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const uint32_t vo = (uint32_t)((4 * (lane >> 5)) * a.ldc + wnu * WN + j * 32 + col_l) * 4u;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            buffer_store_f32(EPI == EPI_RESID ? rv[j][r] + acc[i][j][r] : acc[i][j][r], Ct, cbytes, vo,
+                             (uint32_t)((wmu * WM + i * 32 + 8 * (r / 4) + (r % 4)) * a.ldc) * 4u);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       float rv[FN][16];
@@ -452,9 +496,12 @@ hipError_t launch_epi(const GemmArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_bf16(int epi, const GemmArgs &a, hipStream_t s) {
-  // the loads take 32-bit byte offsets: every weight matrix and any 256 rows
-  // of the activations stay below 4 GiB
-  if ((int64_t)a.N * a.ldb * 2 > 0xFFFFFFFFll || (int64_t)256 * a.lda * 2 > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  // the loads and fp32 stores take 32-bit byte offsets: every weight matrix
+  // and any 256 rows of the activations, the output and the residual stay
+  // below 4 GiB
+  if ((int64_t)a.N * a.ldb * 2 > 0xFFFFFFFFll || (int64_t)256 * a.lda * 2 > 0xFFFFFFFFll ||
+      (int64_t)256 * a.ldc * 4 > 0xFFFFFFFFll || (int64_t)256 * a.ldr * 4 > 0xFFFFFFFFll)
+    return hipErrorInvalidValue;
   switch (epi) {
     case EPI_STORE_F32: return launch_epi<EPI_STORE_F32>(a, s);
     case EPI_RESID: return launch_epi<EPI_RESID>(a, s);
