@@ -8,12 +8,13 @@
 // weight fragment (two MFMAs), so the weight bytes do not change.
 //
 // A block of 8*NR threads owns NR = 64 or 128 B-rows and one K slice
-// (grid.y).  The K slice streams through two LDS stages of 64 k: weights and
-// both activation planes arrive with global_load_lds_dwordx4 in fully
-// coalesced 1 KB pieces (8 rows x 128 bytes), stored with the 16-byte chunk
+// (grid.y).  The K slice streams through NS LDS stages of 64 k: weights and
+// both activation planes arrive with raw buffer loads straight into LDS
+// (buffer_load_dwordx4 ... lds) in fully coalesced 1 KB pieces (8 rows x 128
+// bytes), stored with the 16-byte chunk
 // swizzle c ^ ((row >> 1) & 7) so the MFMA fragment reads of 16 consecutive
 // rows are bank-conflict free.  The activations are shared by all waves
-// through LDS.  Waves w and w + NR/16 own the same 16 B-rows and split each
+// through LDS.  Waves w and w + NR/RW own the same RW B-rows and split each
 // 64-k stage into its two 32-k halves; their partial sums meet in LDS at the
 // end.  Small stages leave room for three 64-row or two 128-row blocks per
 // compute unit: the weight stream is latency-bound, and resident waves, more
@@ -31,6 +32,8 @@
 //                    u = silu(gate) * up written as hi/lo planes [P2 3.5]
 //   SK_LOGITS        fp32 logits (optional) + per-block (max, argmax)
 //                    partials, smallest index on ties [P1 12; P3 4]
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -41,16 +44,28 @@ namespace {
 constexpr int SK_KCH = 64;     // k per LDS stage
 constexpr int SK_ROWB = SK_KCH * 2;  // bytes per tile row (128)
 
-// s_waitcnt vmcnt(n) for a wave-uniform n <= 15 (the count must be an immediate)
+// s_waitcnt vmcnt(n) for a wave-uniform n <= 63 (the count must be an
+// immediate: vmcnt bits 3:0 and 15:14, expcnt and lgkmcnt not waited on)
 __device__ __forceinline__ void wait_vmcnt(int n) {
   switch (n) {
 #define LLK_VM(i) \
-  case i: __builtin_amdgcn_s_waitcnt(0x0F70 | i); break;
-    LLK_VM(0) LLK_VM(1) LLK_VM(2) LLK_VM(3) LLK_VM(4) LLK_VM(5) LLK_VM(6) LLK_VM(7)
-    LLK_VM(8) LLK_VM(9) LLK_VM(10) LLK_VM(11) LLK_VM(12) LLK_VM(13) LLK_VM(14)
+  case i: __builtin_amdgcn_s_waitcnt(0x0F70 | ((i) & 15) | (((i) >> 4) << 14)); break;
+#define LLK_VM8(i) LLK_VM(i) LLK_VM(i + 1) LLK_VM(i + 2) LLK_VM(i + 3) LLK_VM(i + 4) LLK_VM(i + 5) LLK_VM(i + 6) LLK_VM(i + 7)
+    LLK_VM8(0) LLK_VM8(8) LLK_VM8(16) LLK_VM8(24) LLK_VM8(32) LLK_VM8(40) LLK_VM8(48) LLK_VM8(56)
+#undef LLK_VM8
 #undef LLK_VM
-    default: __builtin_amdgcn_s_waitcnt(0x0F70 | 15); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;  // vmcnt(0)
   }
+}
+
+// One 1 KB load into LDS: lane L's 16 bytes at byte voff + soff of the raw
+// buffer [base, base + bytes) (clamped to 4 GiB - 1; reads past the end
+// return zero) land at LDS slot L of dst.
+__device__ __forceinline__ void sk_load_lds(const u16 *base, int64_t bytes, u16 *dst, uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16 *>(base), (short)0, (int)(uint32_t)(bytes < 0xFFFFFFFFll ? bytes : 0xFFFFFFFFll),
+      0x00020000);  // untyped, 32-bit data format, no stride
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
 }
 
 template <int NR, int RW, int NS, int MB, int EPI>
@@ -78,56 +93,66 @@ __global__ __launch_bounds__((NR / RW) * 128) void skinny_kernel(SkinnyArgs a) {
   // never stored.
   static_assert((16 + NR / 8) % NW == 0, "pieces spread evenly over the waves");
   constexpr int NP = (16 + NR / 8) / NW;
+  // The loads are raw buffer loads: a piece's matrix (uniform: an 8-row piece
+  // never straddles two weight matrices, whose boundaries are multiples of
+  // 32 rows) is its resource, a lane's 32-bit offset its row and chunk, and
+  // the chunk's k position goes in the scalar offset.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int lr = lane >> 3, lq = lane & 7;
-  const u16 *src[NP];
+  const u16 *pbase[NP];
+  int64_t pbytes[NP];
+  uint32_t poff[NP];
+  bool pon[NP];  // pieces the MFMAs read
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    const int p = wave + NW * i;
+    const int p = wv + NW * i;
     const int mat = p < 16 ? (p >> 3) : 2;  // 0: A hi, 1: A lo, 2: B
     const int row = mat < 2 ? (p & 7) * 8 + lr : (p - 16) * 8 + lr;  // row of its matrix
     const int c = lq ^ ((row >> 1) & 7);
-    const u16 *base;
-    int64_t ld;
-    int grow;
+    // activation rows from MB*16 on are never read by the MFMAs (few rows:
+    // the prefill LM head, small decode batches), nor is the lo plane of a
+    // one-plane activation: their pieces are skipped
+    pon[i] = !(mat < 2 && ((p & 7) * 8 >= MB * 16 || (mat == 1 && !a.use_lo)));
     if (mat < 2) {
-      grow = min(row, a.M - 1);
-      base = a.A + (mat == 1 && a.use_lo ? a.a_plane : 0);
-      ld = a.lda;
+      pbase[i] = a.A;
+      pbytes[i] = ((int64_t)(a.use_lo ? a.a_plane : 0) + (int64_t)a.M * a.lda) * 2;
+      poff[i] = (uint32_t)(((mat == 1 && a.use_lo ? a.a_plane : 0) + (int64_t)min(row, a.M - 1) * a.lda + kbeg) * 2 +
+                           c * 16);
     } else {
-      int wr;
+      const int prow = (p - 16) * 8;  // the piece's first tile row
+      int wr, sel, nrows;
       if (EPI == SK_SWIGLU_HILO) {
         // tile rows: [gate 0-15 | up 0-15 | gate 16-31 | up 16-31] of this block's 32 output columns
         const int F = a.N / 2;
         wr = min(nblk0 * (NR / 2) + (row >> 5) * 16 + (row & 15), F - 1);
-        base = ((row >> 4) & 1) ? a.B1 : a.B0;
+        sel = (prow >> 4) & 1;
+        nrows = F;
       } else {
         const int n = min(nblk0 * NR + row, a.N - 1);
+        const int np = min(nblk0 * NR + prow, a.N - 1);
         if (a.nq > 0) {
-          base = n < a.nq ? a.B0 : (n < a.nq + a.nk ? a.B1 : a.B2);
+          sel = np < a.nq ? 0 : (np < a.nq + a.nk ? 1 : 2);
           wr = n < a.nq ? n : (n < a.nq + a.nk ? n - a.nq : n - a.nq - a.nk);
+          nrows = sel == 0 ? a.nq : (sel == 1 ? a.nk : a.N - a.nq - a.nk);
         } else {
-          base = a.B0;
+          sel = 0;
           wr = n;
+          nrows = a.N;
         }
       }
-      grow = wr;
-      ld = a.K;
+      // the matrix as an offset from B0 in arithmetic (a select between the
+      // pointer fields would load the argument block at a computed offset)
+      const int64_t d1 = a.B1 - a.B0, d2 = a.B2 - a.B0;
+      pbase[i] = a.B0 + (sel == 1 ? d1 : 0) + (sel == 2 ? d2 : 0);
+      pbytes[i] = (int64_t)nrows * a.K * 2;
+      poff[i] = (uint32_t)(((int64_t)wr * a.K + kbeg) * 2 + c * 16);
     }
-    src[i] = base + (int64_t)grow * ld + kbeg + c * 8;
   }
   auto issue = [&](int stage, int chunk) {
     u16 *st = sm + stage * ST_ELEMS;
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int p = __builtin_amdgcn_readfirstlane(wave + NW * i);
-      // activation rows from MB*16 on are never read by the MFMAs (few rows:
-      // the prefill LM head, small decode batches): their pieces are skipped
-      if (p < 16 && (p & 7) * 8 >= MB * 16) continue;
-      if (p >= 8 && p < 16 && !a.use_lo) continue;  // one activation plane: the lo pieces are never read
-      u16 *dst = st + p * 8 * SK_KCH;
-      __builtin_amdgcn_global_load_lds((const void *)(src[i] + chunk * SK_KCH),
-                                       (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-    }
+    for (int i = 0; i < NP; ++i)
+      if (pon[i]) sk_load_lds(pbase[i], pbytes[i], st + (wv + NW * i) * 8 * SK_KCH, poff[i], (uint32_t)chunk * (SK_KCH * 2));
   };
 
   // fragment offsets: row (lane % 16) of a 16-row block, logical chunk 4*kk + lane/16
@@ -142,41 +167,70 @@ __global__ __launch_bounds__((NR / RW) * 128) void skinny_kernel(SkinnyArgs a) {
   // loads this wave issues per stage (the same for every stage)
   int nper = 0;
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int p = wave + NW * i;
-    nper += !((p < 16 && (p & 7) * 8 >= MB * 16) || (p >= 8 && p < 16 && !a.use_lo));
-  }
+  for (int i = 0; i < NP; ++i) nper += pon[i];
   // NS stages: chunks ch+1 .. ch+NS-1 are in flight while chunk ch is computed
-#pragma unroll
-  for (int c = 0; c < NS - 1; ++c)
-    if (c < nchunk) issue(c, c);
-  for (int ch = 0; ch < nchunk; ++ch) {
-    // this wave's pieces of stage ch have landed (loads complete in order;
-    // the later chunks' pieces may stay in flight); after the barrier every
-    // wave's have, and every wave is done reading the stage refilled next
-    wait_vmcnt(nper * max(0, min(NS - 2, nchunk - 1 - ch)));
+  auto stage = [&](int ch) {
+    // after the barrier every wave's pieces of chunk ch have landed (each
+    // waited for its own before it), and every wave is done reading the
+    // stage refilled next
     asm volatile("s_barrier" ::: "memory");
     if (ch + NS - 1 < nchunk) issue((ch + NS - 1) % NS, ch + NS - 1);
     const u16 *st = sm + (ch % NS) * ST_ELEMS;
     // this wave's 32-k half of the stage, rows rg*RW + 16 j of B (the row
     // swizzle is the same for every 16-row block)
     const int co = ((4 * khalf + (lane >> 4)) ^ sw) * 8;
-    bf16x8 bb[NB];
+    // all fragment reads of the stage first, so their latencies overlap
+    bf16x8 bb[NB], ah[MB], al[MB];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
       bb[j] = *reinterpret_cast<const bf16x8 *>(st + 2 * 64 * SK_KCH + (rg * RW + j * 16 + frow) * SK_KCH + co);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const u16 *ap = st + (mb * 16 + frow) * SK_KCH + co;
-      const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(ap);
+    for (int mb = 0; mb < MB; ++mb) ah[mb] = *reinterpret_cast<const bf16x8 *>(st + (mb * 16 + frow) * SK_KCH + co);
+    if (a.use_lo) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb[j], acc[mb][j], 0, 0, 0);
-      if (a.use_lo) {
-        const bf16x8 al = *reinterpret_cast<const bf16x8 *>(ap + 64 * SK_KCH);
+      for (int mb = 0; mb < MB; ++mb)
+        al[mb] = *reinterpret_cast<const bf16x8 *>(st + (64 + mb * 16 + frow) * SK_KCH + co);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mb], bb[j], acc[mb][j], 0, 0, 0);
+    if (a.use_lo) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb[j], acc[mb][j], 0, 0, 0);
-      }
+          acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[mb], bb[j], acc[mb][j], 0, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < NS - 1; ++c)
+    if (c < nchunk) issue(c, c);
+  // Before chunk ch, this wave waits for its own loads of chunk ch (loads
+  // complete in order; those of the min(NS - 2, nchunk - 1 - ch) later
+  // chunks may stay in flight).  With every piece on (the batched decode) and
+  // at least NS - 2 chunks, every count is a constant: NS - 2 later chunks
+  // until the last NS - 2 chunks, then one fewer each.
+  if (nper == NP && nchunk >= NS - 2) {
+    int ch = 0;
+    for (; ch + NS - 2 < nchunk; ++ch) {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | ((NP * (NS - 2)) & 15) | (((NP * (NS - 2)) >> 4) << 14));
+      stage(ch);
+    }
+    static_assert(NS <= 5, "tail of at most three chunks");
+    auto tail = [&](auto later) {
+      constexpr int n = NP * decltype(later)::value;
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+      stage(ch);
+      ++ch;
+    };
+    if constexpr (NS - 3 >= 2) tail(std::integral_constant<int, 2>{});
+    if constexpr (NS - 3 >= 1) tail(std::integral_constant<int, 1>{});
+    if constexpr (NS - 3 >= 0) tail(std::integral_constant<int, 0>{});
+  } else {
+    for (int ch = 0; ch < nchunk; ++ch) {
+      wait_vmcnt(nper * max(0, min(NS - 2, nchunk - 1 - ch)));
+      stage(ch);
     }
   }
   __syncthreads();  // stages are reused for the epilogue
@@ -329,6 +383,10 @@ int skinny_nblk(int N, int K, int epi) {
 int skinny_ksplit(int N, int K) { return skinny_plan(N, K, SK_PARTIAL).ks; }
 
 hipError_t launch_skinny(int epi, const SkinnyArgs &a, hipStream_t s) {
+  // the loads take 32-bit byte offsets: weights and activation planes below 4 GiB
+  if ((int64_t)a.N * a.K * 2 > 0xFFFFFFFFll ||
+      ((int64_t)(a.use_lo ? a.a_plane : 0) + (int64_t)a.M * a.lda) * 2 > 0xFFFFFFFFll)
+    return hipErrorInvalidValue;
   const Plan p = skinny_plan(a.N, a.K, epi);
   if (epi == SK_PARTIAL && a.ksplit != p.ks) return hipErrorInvalidValue;  // partial planes sized for p.ks
   const dim3 grid(skinny_nblk(a.N, a.K, epi), a.ksplit);
