@@ -9,17 +9,16 @@
 //
 // Tiling: a block of 256 threads (4 waves in a 2x2 grid) owns a BM x BN
 // output tile; each wave owns (BM/2) x (BN/2) as 32x32 MFMA blocks.  The K
-// loop steps through chunks of BK = 32 or 64 held in NS LDS stages.  Tiles
-// move global -> LDS with global_load_lds_dwordx4 (no staging registers): one
-// wave instruction fills 1 KB = 1024 / (2 BK) tile rows, lane L landing at
-// 16-byte slot L.  Each lane fetches the global piece that belongs in its
-// slot under an XOR swizzle (16-byte chunk c of row r lives at chunk
-// c ^ ((r >> SH) & (BK/8 - 1)), SH = 1 for 128-byte rows and 2 for 64-byte
-// rows), so the 16-byte fragment reads of 16 consecutive rows hit 16
+// loop steps through chunks of BK = 32 or 64 held in NS LDS stages (the
+// launches use BK = 64 in two stages).  Tiles move global -> LDS with raw
+// buffer loads straight into LDS (buffer_load_dwordx4 ... lds, no staging
+// registers): one wave instruction fills 1 KB = 1024 / (2 BK) tile rows,
+// lane L landing at 16-byte slot L.  Each lane fetches the global piece that
+// belongs in its slot under an XOR swizzle (16-byte chunk c of row r lives at
+// chunk c ^ ((r >> SH) & (BK/8 - 1)), SH = 1 for 128-byte rows and 2 for
+// 64-byte rows), so the 16-byte fragment reads of 16 consecutive rows hit 16
 // distinct bank groups.  While chunk kt is computed, chunks kt+1 .. kt+NS-1
-// are in flight or landed: the loads of a chunk are issued NS-1 chunks of
-// MFMA work before they are needed, which is what hides the latency of the
-// operands that miss L2.  Operand fragments are double-buffered in
+// are in flight or landed.  Operand fragments are double-buffered in
 // registers across k-steps.
 //
 // MFMA 32x32x16 operand layout (lane l): A supplies row (l % 32) and eight

@@ -11,9 +11,8 @@
 // (grid.y).  The K slice streams through NS LDS stages of 64 k: weights and
 // both activation planes arrive with raw buffer loads straight into LDS
 // (buffer_load_dwordx4 ... lds) in fully coalesced 1 KB pieces (8 rows x 128
-// bytes), stored with the 16-byte chunk
-// swizzle c ^ ((row >> 1) & 7) so the MFMA fragment reads of 16 consecutive
-// rows are bank-conflict free.  The activations are shared by all waves
+// bytes), stored with the 16-byte chunk swizzle c ^ ((row >> 1) & 7) so the
+// MFMA fragment reads of 16 consecutive rows are bank-conflict free.  The activations are shared by all waves
 // through LDS.  Waves w and w + NR/RW own the same RW B-rows and split each
 // 64-k stage into its two 32-k halves; their partial sums meet in LDS at the
 // end.  Small stages leave room for three 64-row or two 128-row blocks per
