@@ -363,43 +363,68 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
     }
     // online softmax of this lane's query, log2 units, lazy rescale (the
     // running maximum moves only when a tile exceeds it by more than 8)
-    float mx = -INFINITY;
+    if (MASK) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (MASK) {
+        for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
           if (key > qpos || (DOC && key < qlo)) sc[kb][r] = -INFINITY;
         }
-        mx = fmaxf(mx, sc[kb][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;
-    if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
-      // finite where the lane has a visible key so far (always without
-      // documents: key 0 is visible to every query)
-      const float m_new = fmaxf(m, mx);
-      float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      // a lane still without a visible key keeps m = -inf (and l = o = 0)
-      if (DOC && m_new == -INFINITY) alpha = 1.f;
-      l *= alpha;
-      m = m_new;
-#pragma unroll
-      for (int i = 0; i < NO; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
     }
     float rs = 0.f;
+    float pw[2][16];
+    auto weights = [&]() {
+      rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -m));
+          // a lane with no visible key yet has m = -inf: its masked scores weigh 0
+          if (DOC && MASK && sc[kb][r] == -INFINITY) p = 0.f;
+          pw[kb][r] = p;
+          rs += p;
+        }
+    };
+    bool need_max = true;
+    if constexpr (!DOC) {
+      // Weights against the running maximum first.  While every lane's
+      // partial row sum stays below 2^7, no weight reaches 2^7, so no score
+      // exceeds the running maximum by 7 and the rescale test below could
+      // not fire: these are the weights the maximum-first order gives.  A
+      // larger sum, inf or NaN (the first tile, where m is still -inf, gives
+      // those) sends the wave through the maximum-first order.
+      weights();
+      need_max = __builtin_amdgcn_ballot_w64(!(rs < 128.f)) != 0;
+    }
+    if (need_max) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;
+      if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
+        // finite where the lane has a visible key so far (always without
+        // documents: key 0 is visible to every query)
+        const float m_new = fmaxf(m, mx);
+        float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        // a lane still without a visible key keeps m = -inf (and l = o = 0)
+        if (DOC && m_new == -INFINITY) alpha = 1.f;
+        l *= alpha;
+        m = m_new;
+#pragma unroll
+        for (int i = 0; i < NO; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      }
+      weights();
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -m));
-        // a lane with no visible key yet has m = -inf: its masked scores weigh 0
-        if (DOC && MASK && sc[kb][r] == -INFINITY) p = 0.f;
-        sc[kb][r] = p;
-        rs += p;
-      }
+      for (int r = 0; r < 16; ++r) sc[kb][r] = pw[kb][r];
     l += rs + __shfl_xor(rs, 32, kWave);
     // O^T += V^T P^T over four 16-key steps
 #pragma unroll
