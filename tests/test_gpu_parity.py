@@ -100,6 +100,88 @@ def test_layer_forward_few_tokens(D, H, G, S, B):
     assert_close(host(xd), ref["y"], BF16_TOL, "layer output in place")
 
 
+# Sharp attention: scores peak at the diagonal, so a row's running maximum
+# jumps when the tile holding its most recent keys arrives.
+SHARP_CASES = [
+    (512, 4, 2, 300, 1, False),  # hd 128 (eight-wave kernel), n_rep 2
+    (512, 4, 2, 300, 1, True),   # the same with three documents
+    (256, 4, 2, 200, 2, False),  # hd 64
+]
+
+
+def sharp_layer(cfg):
+    """Weights and input for which the first query head of each KV group
+    attends sharply to the most recent keys: wq is scaled by 4 (bf16-exact),
+    each group's wk rows copy that head's wq rows, and every input row is one
+    shared row plus small noise.  q_i . k_j then depends mostly on i - j and
+    peaks at j = i.  Returns (layer weights as float32 arrays, x [B, S, D])."""
+    lw = {k: v.copy() for k, v in OR.model_of(cfg).layer(0).items()}
+    hd, rep = cfg.head_dim, cfg.n_heads // cfg.n_kv_heads
+    lw["wq"] = lw["wq"] * np.float32(4.0)
+    for g in range(cfg.n_kv_heads):
+        lw["wk"][g * hd:(g + 1) * hd] = lw["wq"][g * rep * hd:(g * rep + 1) * hd]
+    base = I.hidden_x(cfg)
+    x = base[:1, :1] + np.float32(0.25) * base
+    x = I.bf16_bits_to_f32(I.f32_to_bf16_bits(x))
+    return lw, x
+
+
+def rescales_after_first_tile(q, k, n_rep, doc=None, tile=64):
+    """Rows (head, query) whose running maximum (log2 units, scale 1/sqrt(hd))
+    moves by more than 8 after the row's first visible 64-key tile: where the
+    attention kernels rescale their partial output mid-row."""
+    S, H, hd = q.shape
+    c = np.log2(np.e) / np.sqrt(hd)
+    n = 0
+    for h in range(H):
+        s = (q[:, h] @ k[:, h // n_rep].T) * c
+        for i in range(S):
+            lo = 0 if doc is None else int(np.argmax(doc == doc[i]))
+            m = -np.inf
+            for t0 in range(lo - lo % tile, i + 1, tile):
+                mx = s[i, max(t0, lo):min(t0 + tile, i + 1)].max()
+                if m != -np.inf and mx > m + 8:
+                    n += 1
+                if mx > m + 8:
+                    m = max(m, mx)
+    return n
+
+
+@pytest.mark.parametrize("D,H,G,S,B,docs", SHARP_CASES)
+def test_layer_forward_sharp_attention(D, H, G, S, B, docs):
+    cfg = small_cfg("bf16", D, H, G, S, B)
+    say(f"case layer, sharp attention {cfg.key} S={S} B={B} documents={docs}")
+    lw, x = sharp_layer(cfg)
+    dev = {k: R.bits_to_device(I.f32_to_bf16_bits(v)) for k, v in lw.items()}
+    doc = None
+    if docs:
+        lens = [110, 90, S - 200]
+        doc = np.concatenate([np.full(n, i, np.int32) for i, n in enumerate(lens)])
+        doc = np.tile(doc, (B, 1))
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    kv = R.kv_caches(cfg, 1, B, S)[0]
+    args = R.args_for(cfg, max_batch=B, max_seq=S)
+    ws = R.workspace(args, B, S)
+    if doc is None:
+        M.llama_layer_forward(args, dev, xd, y, B, S, 0, kv=kv, ws=ws)
+    else:
+        M.llama_layer_forward_docs(args, dev, xd, y, B, S, 0, kv=kv, doc_ids=torch.from_numpy(doc).cuda(), ws=ws)
+    torch.cuda.synchronize()
+    a = OR.args_of(cfg)
+    for b in range(B):
+        t = {}
+        if doc is None:
+            ref = OL.layer_forward(x[b], lw, a, np.arange(S), taps=t)
+        else:
+            ref = OL.layer_forward(x[b], lw, a, np.arange(S), taps=t, doc_ids=doc[b])
+        # the inputs really drive the mid-row rescale
+        assert rescales_after_first_tile(t["q"], t["k"], H // G, None if doc is None else doc[b]) >= 20
+        assert_close(host(y[b]), ref, BF16_TOL, f"layer output seq {b}")
+        assert_close(host(kv[0][b]), t["k"], BF16_TOL, f"k cache (rotated) seq {b}")
+        assert_close(host(kv[1][b]), t["v"], BF16_TOL, f"v cache seq {b}")
+
+
 def test_chunked_prefill_few_tokens_per_chunk():
     # three chunks of 20, 12 and 1 positions for 2 sequences, each under 64 tokens
     chunks = [20, 12, 1]
