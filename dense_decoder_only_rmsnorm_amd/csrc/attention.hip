@@ -946,25 +946,6 @@ __global__ __launch_bounds__(256) void attn_decode_mfma2(DecodeAttnArgs a) {
   const int kw0 = c0 + wave * KW;
   const int kmax = kend - 1;  // keys past the end read a valid row; their scores are masked
 
-  // V: 16 direct-to-LDS instructions, 4 rows each; lane L -> row 4i + L/16, chunk L%16
-  u16 *vs = Vs[wave];
-#pragma unroll
-  for (int i = 0; i < KW / 4; ++i) {
-    const int r = 4 * i + (lane >> 4);
-    const int c = (lane & 15) ^ (r & 15);
-    const int key = min(kw0 + r, kmax);
-    __builtin_amdgcn_global_load_lds((const void *)(Vb + (int64_t)key * kstride + c * 8),
-                                     (__attribute__((address_space(3))) void *)(vs + i * 4 * HD), 16, 0, 0);
-  }
-  // K fragments (A operand): key kw0 + 16kb + j, head_dim slice 32t + 8grp
-  uint4 kf[4][NS];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int key = min(kw0 + kb * 16 + j, kmax);
-    const u16 *src = Kb + (int64_t)key * kstride + grp * 8;
-#pragma unroll
-    for (int t = 0; t < NS; ++t) kf[kb][t] = *reinterpret_cast<const uint4 *>(src + t * 32);
-  }
   // query fragments (B operand): column j = head of the group
   bf16x8 qh[NS], ql[NS];
   {
@@ -973,14 +954,46 @@ __global__ __launch_bounds__(256) void attn_decode_mfma2(DecodeAttnArgs a) {
     const int64_t plane = (int64_t)a.B * a.H * HD;
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
-      uint4 h4 = *reinterpret_cast<const uint4 *>(a.qhl + qo + t * 32);
-      uint4 l4 = *reinterpret_cast<const uint4 *>(a.qhl + plane + qo + t * 32);
-      if (j >= n_rep) h4 = l4 = make_uint4(0, 0, 0, 0);
-      qh[t] = __builtin_bit_cast(bf16x8, h4);
-      ql[t] = __builtin_bit_cast(bf16x8, l4);
+      qh[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(a.qhl + qo + t * 32));
+      ql[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(a.qhl + plane + qo + t * 32));
     }
   }
 
+  // K fragments (A operand): key kw0 + 16kb + j, head_dim slice 32t + 8grp;
+  // raw buffer loads over the sequence's rows of the group (32-bit offsets:
+  // the cache block of one sequence is below 4 GiB, checked at launch)
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16 *>(Kb), (short)0, (int)(uint32_t)(((int64_t)a.cap * a.G - g) * HD * 2), 0x00020000);
+  u32x4 kf[4][NS];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const uint32_t key = (uint32_t)min(kw0 + kb * 16 + j, kmax);
+    const uint32_t vo = key * (uint32_t)(kstride * 2) + (uint32_t)(grp * 16);
+#pragma unroll
+    for (int t = 0; t < NS; ++t) kf[kb][t] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo, t * 64, 0);
+  }
+  // V: 16 direct-to-LDS instructions, 4 rows each; lane L -> row 4i + L/16, chunk L%16.
+  // Issued after q and K, so the score products can start while V is in flight.
+  u16 *vs = Vs[wave];
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16 *>(Vb), (short)0, (int)(uint32_t)(((int64_t)a.cap * a.G - g) * HD * 2), 0x00020000);
+#pragma unroll
+  for (int i = 0; i < KW / 4; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    const uint32_t key = (uint32_t)min(kw0 + r, kmax);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void *)(vs + i * 4 * HD), 16,
+                                             key * (uint32_t)(kstride * 2) + (uint32_t)(c * 16), 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load is issued before the first product waits for K
+  if (j >= n_rep) {  // columns past the group's heads (a select on loaded data placed earlier would wait for it)
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      qh[t] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      ql[t] = qh[t];
+    }
+  }
   // S^T (log2 units), masked past the sequence's position
   f32x4 sc[4];
   float mx = -INFINITY;
@@ -1187,9 +1200,11 @@ template <int HD>
 hipError_t decode_hd(int dtype, const DecodeAttnArgs &a, hipStream_t s) {
   dim3 grid(a.nchunk, a.G, a.B);
   const int n_rep = a.H / a.G;
-  if (dtype == 1 && HD == 128 && a.qhl && n_rep <= 4)
+  // attn_decode_mfma2 addresses one sequence's cache block with 32-bit offsets
+  const bool below4g = (int64_t)a.cap * a.G * HD * 2 <= 0xFFFFFFFFll;
+  if (dtype == 1 && HD == 128 && a.qhl && below4g && n_rep <= 4)
     hipLaunchKernelGGL((attn_decode_mfma2<4>), grid, dim3(256), 0, s, a);
-  else if (dtype == 1 && HD == 128 && a.qhl && n_rep <= 16)
+  else if (dtype == 1 && HD == 128 && a.qhl && below4g && n_rep <= 16)
     hipLaunchKernelGGL((attn_decode_mfma2<16>), grid, dim3(256), 0, s, a);
   else if (dtype == 1 && n_rep <= 4)
     hipLaunchKernelGGL((attn_decode_mfma<HD, 4>), grid, dim3(256), 0, s, a);
