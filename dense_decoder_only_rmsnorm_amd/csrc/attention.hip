@@ -759,33 +759,45 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(DecodeAttnArgs a) {
   const u16 *Vb = static_cast<const u16 *>(a.v) + ((int64_t)b * a.cap * a.G + g) * HD;
   const int kw0 = c0 + wave * KW;
 
-  // issue every load of this wave first: K fragments and V pieces
+  // issue every load of this wave first: K fragments and V pieces.  Keys past
+  // the end read the last visible row (their scores are masked, their
+  // weights are 0) and lanes past the head dimension read its last piece
+  // (never stored), so no load waits on a select of its data.
+  const int kmax = kend - 1;
   uint4 kf[4][NS];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const int key = kw0 + kb * 16 + j;
-    const bool ok = key < kend;
-    const u16 *src = Kb + (int64_t)(ok ? key : 0) * kstride + grp * 8;
+    const u16 *src = Kb + (int64_t)min(kw0 + kb * 16 + j, kmax) * kstride + grp * 8;
 #pragma unroll
-    for (int t = 0; t < NS; ++t) kf[kb][t] = ok ? *reinterpret_cast<const uint4 *>(src + t * 32) : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < NS; ++t) kf[kb][t] = *reinterpret_cast<const uint4 *>(src + t * 32);
   }
   uint4 vf[16];
+  const int jc = min(j, NDC - 1);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int key = kw0 + i * 4 + grp;
-    const bool ok = key < kend && j < NDC;
-    vf[i] = ok ? *reinterpret_cast<const uint4 *>(Vb + (int64_t)key * kstride + j * 8) : make_uint4(0, 0, 0, 0);
-  }
+  for (int i = 0; i < 16; ++i)
+    vf[i] = *reinterpret_cast<const uint4 *>(Vb + (int64_t)min(kw0 + i * 4 + grp, kmax) * kstride + jc * 8);
 
   // query fragments (B operand): column j = head of the group, k = head_dim
   const float c = a.scale * kLog2e;
   bf16x8 qh[NS], ql[NS];
+  // every lane loads (columns past the group's heads from head 0) and zeroes
+  // afterwards, so the loads are issued together rather than one per branch
+  float4 qv[NS][2];
+  {
+    const float *qrow = a.q + ((int64_t)b * a.H + g * n_rep + (j < n_rep ? j : 0)) * HD + grp * 8;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      qv[t][0] = *reinterpret_cast<const float4 *>(qrow + t * 32);
+      qv[t][1] = *reinterpret_cast<const float4 *>(qrow + t * 32 + 4);
+    }
+  }
 #pragma unroll
   for (int t = 0; t < NS; ++t) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float v = 0.f;
-      if (j < n_rep) v = a.q[((int64_t)b * a.H + g * n_rep + j) * HD + t * 32 + grp * 8 + e] * c;
+      const float4 q4 = qv[t][e >> 2];
+      const float qe = (e & 3) == 0 ? q4.x : (e & 3) == 1 ? q4.y : (e & 3) == 2 ? q4.z : q4.w;
+      const float v = j < n_rep ? qe * c : 0.f;
       u16 hi, lo;
       split_hilo(v, hi, lo);
       qh[t][e] = __builtin_bit_cast(__bf16, hi);
