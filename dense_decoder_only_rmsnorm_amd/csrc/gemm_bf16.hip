@@ -281,24 +281,33 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
       const float *Rt = a.R + (int64_t)m0 * a.ldr + n0;
       float *Ct = C + (int64_t)m0 * a.ldc + n0;
       const int64_t rbytes = ((int64_t)(a.M - m0) * a.ldr - n0) * 4, cbytes = ((int64_t)(a.M - m0) * a.ldc - n0) * 4;
+      // The residual rows of 32-row block i+1 are loaded before block i is
+      // stored: the output may be the residual itself, so a load placed
+      // after a store would wait for that store to complete.
+      float rv[2][FN][16];
+      auto load_block = [&](int i, auto buf_c) {
+        constexpr int BUF = decltype(buf_c)::value;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const uint32_t vo = (uint32_t)((4 * (lane >> 5)) * a.ldr + wnu * WN + j * 32 + col_l) * 4u;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            rv[BUF][j][r] = buffer_load_f32(Rt, rbytes, vo, (uint32_t)((wmu * WM + i * 32 + 8 * (r / 4) + (r % 4)) * a.ldr) * 4u);
+        }
+      };
+      if (EPI == EPI_RESID) load_block(0, std::integral_constant<int, 0>());
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        float rv[FN][16];
-        if (EPI == EPI_RESID) {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const uint32_t vo = (uint32_t)((4 * (lane >> 5)) * a.ldr + wnu * WN + j * 32 + col_l) * 4u;
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              rv[j][r] = buffer_load_f32(Rt, rbytes, vo, (uint32_t)((wmu * WM + i * 32 + 8 * (r / 4) + (r % 4)) * a.ldr) * 4u);
-          }
+        if (EPI == EPI_RESID && i + 1 < FM) {
+          if (i & 1) load_block(i + 1, std::integral_constant<int, 0>());
+          else load_block(i + 1, std::integral_constant<int, 1>());
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const uint32_t vo = (uint32_t)((4 * (lane >> 5)) * a.ldc + wnu * WN + j * 32 + col_l) * 4u;
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            buffer_store_f32(EPI == EPI_RESID ? rv[j][r] + acc[i][j][r] : acc[i][j][r], Ct, cbytes, vo,
+            buffer_store_f32(EPI == EPI_RESID ? rv[i & 1][j][r] + acc[i][j][r] : acc[i][j][r], Ct, cbytes, vo,
                              (uint32_t)((wmu * WM + i * 32 + 8 * (r / 4) + (r % 4)) * a.ldc) * 4u);
         }
       }

@@ -5,6 +5,8 @@
 // Pages: [P1] llama3-from-scratch translation (sections 4, 5, 6.6-6.9, 9.3, 12);
 //        [P2] "Build your own Llama 3" notes (sections 3.1-3.5);
 //        [P3] llama3-from-scratch output layer page (steps 1-4).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -61,19 +63,28 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
 // (decode) use NT = 1024 so that the partial planes stream with enough
 // loads in flight.
 // ---------------------------------------------------------------------------
-template <typename TW, int MODE, int NT>
+template <typename TW, int MODE, int NT, int NV>
 __global__ __launch_bounds__(NT) void rmsnorm_kernel(NormArgs a) {
-  constexpr int MAXV = 8192 / (NT * 4);
+  // NV > 0: D is exactly NV * NT * 4, every lane holds NV pieces and no
+  // piece needs a guard (the guards' branches make the compiler wait for
+  // each store before the next); NV == 0: any D <= 8192
+  constexpr int MAXV = NV > 0 ? NV : 8192 / (NT * 4);
   const int r = blockIdx.x;
   const int D = a.D;
   float *x = a.h + a.in_offset + (int64_t)r * a.in_stride;
   float4 v[MAXV];
   float ss = 0.f;
+  // the row's loads first, all in flight together; then the folds and sums
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     const int i = (j * NT + threadIdx.x) * 4;
-    if (i < D) {
-      float4 t = *reinterpret_cast<const float4 *>(x + i);
+    if (NV > 0 || i < D) v[j] = *reinterpret_cast<const float4 *>(x + i);
+  }
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int i = (j * NT + threadIdx.x) * 4;
+    if (NV > 0 || i < D) {
+      float4 t = v[j];
       if (a.nsplit > 0) {
         // partials in groups of 8: the group's loads (clamped to a valid
         // plane, the extra ones weighted 0) are issued together instead of
@@ -107,14 +118,25 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(NormArgs a) {
     scale = 1.0f / sqrtf(tot / (float)D + a.eps);
   }
   const TW *w = static_cast<const TW *>(a.w);
+  // all weight loads (raw 4-element pieces, converted at their use) before
+  // the first store: a store the compiler cannot tell apart from the weights
+  // would make every later load wait for it
+  using WRaw = typename std::conditional<std::is_same<TW, float>::value, float4, uint2>::type;
+  WRaw wraw[MAXV];
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     const int i = (j * NT + threadIdx.x) * 4;
-    if (i < D) {
+    if (w != nullptr && (NV > 0 || i < D)) wraw[j] = *reinterpret_cast<const WRaw *>(w + i);
+  }
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int i = (j * NT + threadIdx.x) * 4;
+    if (NV > 0 || i < D) {
       float y[4] = {v[j].x * scale, v[j].y * scale, v[j].z * scale, v[j].w * scale};
       if (w != nullptr) {
+        const TW *we = reinterpret_cast<const TW *>(&wraw[j]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] *= Elem<TW>::load(w + i + e);
+        for (int e = 0; e < 4; ++e) y[e] *= Elem<TW>::load(we + e);
       }
       const int64_t o = (int64_t)r * D + i;
       if (MODE == 0) {
@@ -324,10 +346,14 @@ hipError_t launch_embed(int dtype, const int32_t *ids, const void *E, float *h, 
 hipError_t launch_rmsnorm(int dtype, int mode, const NormArgs &a, int rows, hipStream_t s) {
 #define LLK_NORM(TW, M)                                                                           \
   do {                                                                                            \
-    if (rows < 512)                                                                               \
-      hipLaunchKernelGGL((rmsnorm_kernel<TW, M, 1024>), dim3(rows), dim3(1024), 0, s, a);        \
+    if (rows < 512 && a.D == 4096)                                                                \
+      hipLaunchKernelGGL((rmsnorm_kernel<TW, M, 1024, 1>), dim3(rows), dim3(1024), 0, s, a);     \
+    else if (rows < 512)                                                                          \
+      hipLaunchKernelGGL((rmsnorm_kernel<TW, M, 1024, 0>), dim3(rows), dim3(1024), 0, s, a);     \
+    else if (a.D == 4096)                                                                         \
+      hipLaunchKernelGGL((rmsnorm_kernel<TW, M, 256, 4>), dim3(rows), dim3(256), 0, s, a);       \
     else                                                                                          \
-      hipLaunchKernelGGL((rmsnorm_kernel<TW, M, 256>), dim3(rows), dim3(256), 0, s, a);          \
+      hipLaunchKernelGGL((rmsnorm_kernel<TW, M, 256, 0>), dim3(rows), dim3(256), 0, s, a);       \
   } while (0)
   if (dtype == 0) {
     if (mode == 0) LLK_NORM(float, 0);
