@@ -591,13 +591,28 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
     }
   }
   const int col = n0 + wn * 32 + fr;
+  // the residual loads (from clamped, valid rows and columns) all before the
+  // first store: the output may be the residual itself
+  float rv[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = m0 + wm * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
-    if (row < M && col < N) {
-      const float v = acc0[r] + acc1[r];
-      C[(int64_t)row * ldc + col] = R ? R[(int64_t)row * ldr + col] + v : v;
-    }
+    rv[r] = R ? R[(int64_t)min(row, M - 1) * ldr + min(col, N - 1)] : 0.f;
+  }
+  // the sums formed before the guarded stores (the empty asm keeps the
+  // compiler from sinking them into the branches), so that no store's branch
+  // waits for the loads again
+  float out[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float v = acc0[r] + acc1[r];
+    out[r] = R ? rv[r] + v : v;
+    asm volatile("" : "+v"(out[r]));
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + wm * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+    if (row < M && col < N) C[(int64_t)row * ldc + col] = out[r];
   }
 }
 }  // namespace

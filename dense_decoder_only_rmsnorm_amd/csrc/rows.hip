@@ -78,6 +78,7 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(NormArgs a) {
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     const int i = (j * NT + threadIdx.x) * 4;
+    v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (NV > 0 || i < D) v[j] = *reinterpret_cast<const float4 *>(x + i);
   }
 #pragma unroll
@@ -126,18 +127,32 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(NormArgs a) {
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     const int i = (j * NT + threadIdx.x) * 4;
+    wraw[j] = WRaw{};
     if (w != nullptr && (NV > 0 || i < D)) wraw[j] = *reinterpret_cast<const WRaw *>(w + i);
+  }
+  // the outputs are formed before the guarded stores (the empty asm keeps
+  // the compiler from sinking them into the branches, where each would wait
+  // for the loads and for the previous store again)
+  float yv[MAXV][4];
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    yv[j][0] = v[j].x * scale;
+    yv[j][1] = v[j].y * scale;
+    yv[j][2] = v[j].z * scale;
+    yv[j][3] = v[j].w * scale;
+    if (w != nullptr) {
+      const TW *we = reinterpret_cast<const TW *>(&wraw[j]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yv[j][e] *= Elem<TW>::load(we + e);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(yv[j][e]));
   }
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     const int i = (j * NT + threadIdx.x) * 4;
     if (NV > 0 || i < D) {
-      float y[4] = {v[j].x * scale, v[j].y * scale, v[j].z * scale, v[j].w * scale};
-      if (w != nullptr) {
-        const TW *we = reinterpret_cast<const TW *>(&wraw[j]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] *= Elem<TW>::load(we + e);
-      }
+      const float *y = yv[j];
       const int64_t o = (int64_t)r * D + i;
       if (MODE == 0) {
         *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + o) = make_float4(y[0], y[1], y[2], y[3]);
