@@ -1120,6 +1120,28 @@ __global__ __launch_bounds__(((HD + 63) / 64) * 64) void attn_combine_kernel(Dec
   const bool on = t < HD;
   const int d = on ? t : HD - 1;
   const int64_t base = ((int64_t)b * a.H + h) * a.nchunk;
+  // Only chunks that hold visible keys are merged: keys 0..pos-1 when the
+  // own term is added here, 0..pos otherwise (the chunk kernels leave the
+  // others empty).  They are merged 16 at a time: each group's loads
+  // (clamped to a valid chunk; the extra ones are skipped) are issued
+  // together, and the running maximum M rescales what earlier groups summed.
+  // The first group's loads go out before the own term's dot product.
+  int pb = a.pos[b];
+  pb = pb < 0 ? 0 : (pb > a.cap - 1 ? a.cap - 1 : pb);
+  const int nkeys = a.knew ? pb : pb + 1;
+  const int nc = min(a.nchunk, (nkeys + a.chunk - 1) / a.chunk);
+  constexpr int CG = 16;
+  float pm[CG], pl[CG], po[CG];
+  auto load_group = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < CG; ++u) {
+      const int64_t c = base + max(0, min(c0 + u, nc - 1));
+      pm[u] = a.pm[c];
+      pl[u] = a.pl[c];
+      po[u] = a.po[c * HD + d];
+    }
+  };
+  load_group(0);
   float ms = -INFINITY, vself = 0.f;
   if (a.knew) {
     const int g = h / (a.H / a.G);
@@ -1134,30 +1156,13 @@ __global__ __launch_bounds__(((HD + 63) / 64) * 64) void attn_combine_kernel(Dec
     ms = dot * a.scale * kLog2e;
     vself = a.vnew[kv];
   }
-  // Only chunks that hold visible keys are merged: keys 0..pos-1 when the
-  // own term is added here, 0..pos otherwise (the chunk kernels leave the
-  // others empty).  They are merged 16 at a time: each group's loads
-  // (clamped to a valid chunk; the extra ones are skipped) are issued
-  // together, and the running maximum M rescales what earlier groups summed.
   float M = ms, L = 0.f, acc = 0.f;
   if (a.knew) {
     L = 1.f;
     acc = vself;
   }
-  int pb = a.pos[b];
-  pb = pb < 0 ? 0 : (pb > a.cap - 1 ? a.cap - 1 : pb);
-  const int nkeys = a.knew ? pb : pb + 1;
-  const int nc = min(a.nchunk, (nkeys + a.chunk - 1) / a.chunk);
-  constexpr int CG = 16;
   for (int c0 = 0; c0 < nc; c0 += CG) {
-    float pm[CG], pl[CG], po[CG];
-#pragma unroll
-    for (int u = 0; u < CG; ++u) {
-      const int64_t c = base + min(c0 + u, nc - 1);
-      pm[u] = a.pm[c];
-      pl[u] = a.pl[c];
-      po[u] = a.po[c * HD + d];
-    }
+    if (c0 > 0) load_group(c0);
     float Mg = M;
 #pragma unroll
     for (int u = 0; u < CG; ++u)
