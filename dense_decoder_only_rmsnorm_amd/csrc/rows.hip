@@ -29,8 +29,20 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
   const bool ok = id >= 0 && id < V;
   const TW *src = E + (int64_t)(ok ? id : 0) * D;
   const float qnan = __int_as_float(0x7fc00000);
-  for (int i = threadIdx.x * EPL; i < D; i += 256 * EPL) {
-    const uint4 raw = ok ? *reinterpret_cast<const uint4 *>(src + i) : make_uint4(0, 0, 0, 0);
+  // every piece of the row is loaded before the first store (D <= 8192)
+  constexpr int MAXP = 8192 / (256 * EPL);
+  uint4 raws[MAXP];
+#pragma unroll
+  for (int k = 0; k < MAXP; ++k) {
+    const int i = (k * 256 + threadIdx.x) * EPL;
+    raws[k] = make_uint4(0, 0, 0, 0);
+    if (i < D) raws[k] = *reinterpret_cast<const uint4 *>(src + i);
+  }
+#pragma unroll
+  for (int k = 0; k < MAXP; ++k) {
+    const int i = (k * 256 + threadIdx.x) * EPL;
+    if (i >= D) break;
+    const uint4 raw = raws[k];
     if (EPL == 8) {
       const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
       float4 lo, hi;
@@ -219,6 +231,16 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(RopeQkvArgs a) {
   const int r = (int)(idx / npair);
   const int j = (int)(idx % npair) * 2;  // even column
   const int N = (a.H + 2 * a.G) * a.hd;
+  const int Hq = a.H * a.hd, Hk = a.G * a.hd;
+  const int b = r / a.S, sidx = r % a.S;
+  // the loads that do not depend on the partial sums go out first: the
+  // sequence's position and the table entry (v columns read a valid entry
+  // and keep their values)
+  int p0 = a.pos ? a.pos[b] : a.start_pos;
+  const int tr = a.tab_mod > 0 ? (r % a.tab_mod) : r;
+  const bool rot = j < Hq + Hk;
+  const int dcol = (j < Hq ? j : (rot ? j - Hq : 0)) % a.hd;
+  const float2 cs = a.tab[(int64_t)tr * (a.hd / 2) + dcol / 2];
   float x0 = 0.f, x1 = 0.f;
   for (int s0 = 0; s0 < a.nsplit; s0 += 8) {  // loads of 8 partials at a time (see rmsnorm_kernel)
     float2 t[8];
@@ -232,19 +254,13 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(RopeQkvArgs a) {
       x1 += m * t[u].y;
     }
   }
-  const int b = r / a.S, sidx = r % a.S;
-  int p0 = a.pos ? a.pos[b] : a.start_pos;
   p0 = p0 < 0 ? 0 : (p0 > a.cap - 1 ? a.cap - 1 : p0);
   int p = p0 + sidx;
   p = p > a.cap - 1 ? a.cap - 1 : p;
-  const int Hq = a.H * a.hd, Hk = a.G * a.hd;
-  const int tr = a.tab_mod > 0 ? (r % a.tab_mod) : r;
-  if (j < Hq + Hk) {
-    const int d = (j < Hq ? j : j - Hq) % a.hd;
-    const float2 cs = a.tab[(int64_t)tr * (a.hd / 2) + d / 2];
+  {
     const float2 y = rotate_pair(x0, x1, cs.x, cs.y);
-    x0 = y.x;
-    x1 = y.y;
+    x0 = rot ? y.x : x0;
+    x1 = rot ? y.y : x1;
   }
   if (j < Hq) {
     if (a.qout) *reinterpret_cast<float2 *>(a.qout + (int64_t)r * Hq + j) = make_float2(x0, x1);
