@@ -361,6 +361,22 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cb][kb], qf[t], sc[kb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    // V^T fragments of the first 16-key step, read before the softmax so the
+    // first P.V products need not wait for them (non-document kernel)
+    u32x2 wv0[NO][2];
+    if constexpr (!DOC) {
+#pragma unroll
+      for (int ob = 0; ob < NO; ++ob)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const v4s w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s *)(const __attribute__((address_space(3))) u16 *)(vs + vofs[ob][h2]));
+          wv0[ob][h2] = __builtin_bit_cast(u32x2, w);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // online softmax of this lane's query, log2 units, lazy rescale (the
     // running maximum moves only when a tile exceeds it by more than 8)
     if (MASK) {
@@ -435,11 +451,13 @@ __global__ __launch_bounds__(512) void attn_fwd_w8(AttnArgs a) {
       for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sc[kb][8 * t + e];
 #pragma unroll
       for (int ob = 0; ob < NO; ++ob) {
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
         u32x2 wv[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
+          if (!DOC && ksp == 0) {
+            wv[h2] = wv0[ob][h2];
+            continue;
+          }
           const u16 *src = vs + vofs[ob][h2] + 16 * ksp * HD;
           const v4s w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) v4s *)(const __attribute__((address_space(3))) u16 *)src);
