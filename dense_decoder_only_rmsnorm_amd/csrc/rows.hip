@@ -86,12 +86,39 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(NormArgs a) {
   float *x = a.h + a.in_offset + (int64_t)r * a.in_stride;
   float4 v[MAXV];
   float ss = 0.f;
-  // the row's loads first, all in flight together; then the folds and sums
+  // the row's loads and the weight loads first, all in flight together (a
+  // store the compiler cannot tell apart from the weights would make every
+  // later load wait for it); then the folds and sums
+  const TW *w = static_cast<const TW *>(a.w);
+  using WRaw = typename std::conditional<std::is_same<TW, float>::value, float4, uint2>::type;
+  WRaw wraw[MAXV];  // raw 4-element pieces, converted at their use
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     const int i = (j * NT + threadIdx.x) * 4;
     v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (NV > 0 || i < D) v[j] = *reinterpret_cast<const float4 *>(x + i);
+    // (without weights the row itself is read in their place and ignored, so
+    // the load is not behind a branch that would wait for it)
+    const WRaw *wp = w != nullptr ? reinterpret_cast<const WRaw *>(w + i) : reinterpret_cast<const WRaw *>(x + i);
+    wraw[j] = WRaw{};
+    if (NV > 0 || i < D) wraw[j] = *wp;
+  }
+  // Split-K partials in groups of 8: a group's loads (clamped to a valid
+  // plane, the extra ones weighted 0) are issued together instead of one
+  // latency per plane.  The few-row (decode) variants issue the first group
+  // with the row loads above, ahead of the loop.
+  constexpr int PG = NT == 1024 ? MAXV : 1;
+  float4 p0[PG][8];
+  if (NT == 1024 && a.nsplit > 0) {
+#pragma unroll
+    for (int j = 0; j < PG; ++j) {
+      const int i = (j * NT + threadIdx.x) * 4;
+      if (NV > 0 || i < D) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          p0[j][u] = *reinterpret_cast<const float4 *>(a.part + min(u, a.nsplit - 1) * a.part_stride + (int64_t)r * D + i);
+      }
+    }
   }
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
@@ -99,14 +126,16 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(NormArgs a) {
     if (NV > 0 || i < D) {
       float4 t = v[j];
       if (a.nsplit > 0) {
-        // partials in groups of 8: the group's loads (clamped to a valid
-        // plane, the extra ones weighted 0) are issued together instead of
-        // one latency per plane
         for (int s0 = 0; s0 < a.nsplit; s0 += 8) {
           float4 p[8];
+          if (NT == 1024 && s0 == 0) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            p[u] = *reinterpret_cast<const float4 *>(a.part + min(s0 + u, a.nsplit - 1) * a.part_stride + (int64_t)r * D + i);
+            for (int u = 0; u < 8; ++u) p[u] = p0[j < PG ? j : 0][u];
+          } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              p[u] = *reinterpret_cast<const float4 *>(a.part + min(s0 + u, a.nsplit - 1) * a.part_stride + (int64_t)r * D + i);
+          }
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             const float m = s0 + u < a.nsplit ? 1.f : 0.f;
@@ -129,18 +158,6 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(NormArgs a) {
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) tot += red[w];
     scale = 1.0f / sqrtf(tot / (float)D + a.eps);
-  }
-  const TW *w = static_cast<const TW *>(a.w);
-  // all weight loads (raw 4-element pieces, converted at their use) before
-  // the first store: a store the compiler cannot tell apart from the weights
-  // would make every later load wait for it
-  using WRaw = typename std::conditional<std::is_same<TW, float>::value, float4, uint2>::type;
-  WRaw wraw[MAXV];
-#pragma unroll
-  for (int j = 0; j < MAXV; ++j) {
-    const int i = (j * NT + threadIdx.x) * 4;
-    wraw[j] = WRaw{};
-    if (w != nullptr && (NV > 0 || i < D)) wraw[j] = *reinterpret_cast<const WRaw *>(w + i);
   }
   // the outputs are formed before the guarded stores (the empty asm keeps
   // the compiler from sinking them into the branches, where each would wait
