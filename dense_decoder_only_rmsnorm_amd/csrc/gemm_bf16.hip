@@ -58,6 +58,29 @@ __device__ __forceinline__ void buffer_store_f32(float v, float *base, int64_t b
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
 }
 
+// Copy-out of a whole staged tile: thread tid moves the 16-byte piece at
+// column c8 of every (256 / CPR)-th row from LDS to dst + row * ld.  The LDS
+// reads go out in batches of eight before their stores (one read-wait-store
+// per row otherwise; the empty asm keeps the stores behind the batch).
+template <int BM, int CPR, int LDC>
+__device__ __forceinline__ void copy_whole_tile(const u16 *Cs, int tid, int c8, u16 *dst, int64_t ld) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int STEP = 256 / CPR, NIT = BM / STEP, NB = NIT < 8 ? NIT : 8;
+  const int r0 = tid / CPR;
+  u16 *dr = dst + r0 * ld;
+  const int64_t rstep = STEP * ld;
+#pragma unroll
+  for (int i0 = 0; i0 < NIT; i0 += NB) {
+    u32x4 v[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) v[u] = *reinterpret_cast<const u32x4 *>(Cs + (r0 + (i0 + u) * STEP) * LDC + c8);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) asm volatile("" : "+v"(v[u]));
+#pragma unroll
+    for (int u = 0; u < NB; ++u) *reinterpret_cast<u32x4 *>(dr + (i0 + u) * rstep) = v[u];
+  }
+}
+
 template <int BM, int BN, int BK, int NS, int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WM = BM / 2, WN = BN / 2;
@@ -452,6 +475,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   if (EPI == EPI_QKV_ROPE) {
     const int Hq = a.H * a.hd, Hk = a.G * a.hd;
     if (col < Hq) {
+      if (m0 + BM <= a.M) {
+        copy_whole_tile<BM, CPR, LDC>(Cs, tid, c8, a.q + (int64_t)m0 * Hq + col, Hq);
+        return;
+      }
       for (int rr = tid / CPR; rr < BM && m0 + rr < a.M; rr += 256 / CPR)
         *reinterpret_cast<uint4 *>(a.q + (int64_t)(m0 + rr) * Hq + col) =
             *reinterpret_cast<const uint4 *>(Cs + rr * LDC + c8);
@@ -479,6 +506,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     return;
   }
   u16 *C = static_cast<u16 *>(a.C) + col;
+  if (m0 + BM <= a.M) {
+    copy_whole_tile<BM, CPR, LDC>(Cs, tid, c8, C + (int64_t)m0 * a.ldc, a.ldc);
+    return;
+  }
   for (int rr = tid / CPR; rr < BM && m0 + rr < a.M; rr += 256 / CPR)
     *reinterpret_cast<uint4 *>(C + (int64_t)(m0 + rr) * a.ldc) = *reinterpret_cast<const uint4 *>(Cs + rr * LDC + c8);
 }
