@@ -79,9 +79,12 @@ __global__ __launch_bounds__((NR / RW) * 128) void skinny_kernel(SkinnyArgs a) {
   const int rg = wave % NG, khalf = wave / NG;
   const int nblk0 = blockIdx.x;
   const int ks = blockIdx.y;
-  const int Kc = a.K / a.ksplit;
-  const int kbeg = ks * Kc;
-  const int nchunk = Kc / SK_KCH;
+  // K slice ks: chunks [ks*T/ksplit, (ks+1)*T/ksplit) of the T = K/64 (the
+  // slices differ by at most one chunk when ksplit does not divide T)
+  const int T = a.K / SK_KCH;
+  const int cbeg = ks * T / a.ksplit;
+  const int kbeg = cbeg * SK_KCH;
+  const int nchunk = (ks + 1) * T / a.ksplit - cbeg;
 
   // Loader: 16 + NR/8 pieces of 1 KB per stage (A hi 8, A lo 8, B NR/8),
   // piece p at stage offset 512*p; wave w issues pieces w, w + NW, ...
@@ -355,7 +358,10 @@ int ksplit_rule(int nblk, int K) {
 // computed) streams fastest when the blocks fill one round of the chip
 // (w1/w3 70 -> 58.5 us, w2 30.9 -> 27.8 us, wo 14.5 -> 12.5 us); products
 // with more row blocks than that keep two stages and about 1.5 blocks per
-// compute unit, as does the LM head (1002 blocks).
+// compute unit, as does the LM head (1002 blocks).  The K split of a
+// one-round plan is the largest that keeps the blocks within 256 and every
+// slice at 256 k or more, whether or not it divides K (the QKV product's 48
+// row blocks take 5 slices, 240 blocks, instead of 4).
 struct Plan {
   int nr, rw, ns, ks;
 };
@@ -365,7 +371,7 @@ Plan skinny_plan(int N, int K, int epi) {
   if (epi == SK_SWIGLU_HILO) return {128, 32, 4, 1};
   const int nb = (N + 127) / 128;
   int ks = 1;
-  while (nb * ks * 2 <= 256 && K % (ks * 2 * SK_KCH) == 0 && K / (ks * 2) >= 256) ks *= 2;
+  while (nb * (ks + 1) <= 256 && K / SK_KCH / (ks + 1) >= 4) ++ks;
   if (nb * ks >= 192) return {128, 32, 4, ks};
   const int nr = K / ksplit_rule(nb, K) >= 256 ? 128 : 64;
   return {nr, 16, 2, ksplit_rule((N + nr - 1) / nr, K)};
